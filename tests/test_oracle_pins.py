@@ -1,0 +1,414 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: each checks it against a library
+routine it reduces to, a closed form, an invariant, brute force on tiny
+inputs, or a value printed on the pages (tests/golden/).  The mutation tests at
+the end plant plausible mistakes in a copy of the oracle and check that a pin
+catches each of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from sparse_long_context_index_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- O0 decode
+
+def test_e4m3_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    got = oracle.decode_e4m3(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+    assert np.array_equal(np.signbit(got[m]), np.signbit(ref[m]))
+
+
+def test_e4m3_spec_points():
+    for line in open(os.path.join(GOLDEN, "e4m3_spec_points.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = oracle.decode_e4m3(np.array([int(code, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == float(val) and np.signbit(got) == val.startswith("-")
+
+
+def test_bf16_all_codes_match_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode_bf16(bits)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+
+
+# ------------------------------------------------------- O2/O3 index scores
+
+def _codes(rng, shape, lo=0, hi=256, finite=True):
+    c = rng.integers(lo, hi, size=shape).astype(np.uint8)
+    if finite:
+        c[(c & 0x7F) == 0x7F] = 0x3F
+    return c
+
+
+def test_index_logits_exact_integer_recompute():
+    rng = np.random.default_rng(0)
+    q = _codes(rng, (3, 16, 128))
+    k = _codes(rng, (50, 128))
+    # independent integer path: torch's fp8 decode, scaled by 2^9 to integers
+    qi = (torch.from_numpy(q).view(torch.float8_e4m3fn).double() * 512).numpy()
+    ki = (torch.from_numpy(k).view(torch.float8_e4m3fn).double() * 512).numpy()
+    assert np.all(qi == np.round(qi)) and np.all(ki == np.round(ki))
+    exact = np.einsum("thd,sd->ths", qi.astype(np.int64), ki.astype(np.int64))
+    got = oracle.index_logits(q, k) * 2.0 ** 18
+    assert np.array_equal(got, exact.astype(np.float64))
+    # extreme magnitudes: every code 448 -> 128 * 448^2
+    big = np.full((1, 16, 128), 0x7E, dtype=np.uint8)
+    assert oracle.index_logits(big, np.full((2, 128), 0x7E, np.uint8))[0, 0, 0] == 128 * 448.0 ** 2
+
+
+def test_index_scores_brute_force_with_causal_mask():
+    rng = np.random.default_rng(1)
+    T, Lk = 3, 9
+    q = _codes(rng, (T, 16, 128))
+    k = _codes(rng, (Lk, 128))
+    w = rng.standard_normal((T, 16)).astype(np.float32)
+    got = oracle.index_scores(q, w, k, Lk, T)
+    qd = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    kd = torch.from_numpy(k).view(torch.float8_e4m3fn).double().numpy()
+    for t in range(T):
+        for s in range(Lk):
+            if s > Lk - T + t:
+                assert got[t, s] == -np.inf
+                continue
+            acc = 0.0
+            for h in range(16):
+                dot = 0.0
+                for d in range(128):
+                    dot += qd[t, h, d] * kd[s, d]
+                acc += float(w[t, h]) * max(dot, 0.0)
+            assert got[t, s] == pytest.approx(acc, rel=1e-12, abs=1e-12)
+
+
+def test_index_scores_closed_forms():
+    rng = np.random.default_rng(2)
+    qrow = _codes(rng, (128,))
+    q = np.broadcast_to(qrow, (1, 16, 128)).copy()          # 16 identical heads
+    k = _codes(rng, (40, 128))
+    Lk = 40
+    ones = np.ones((1, 16), dtype=np.float32)
+    s1 = oracle.index_scores(q, ones, k, Lk, 1)[0]
+    dots = oracle.decode_e4m3(k) @ oracle.decode_e4m3(qrow)
+    assert np.array_equal(s1, 16.0 * np.maximum(dots, 0.0))
+    # flipping every weight flips every score
+    w = rng.standard_normal((1, 16)).astype(np.float32)
+    q2 = _codes(rng, (1, 16, 128))
+    a = oracle.index_scores(q2, w, k, Lk, 1)
+    b = oracle.index_scores(q2, -w, k, Lk, 1)
+    assert np.array_equal(a, -b)
+    # a key anti-aligned with every head scores exactly zero
+    qpos = np.full((1, 16, 128), 0x38, dtype=np.uint8)       # all +1.0
+    kneg = np.full((3, 128), 0xB8, dtype=np.uint8)           # all -1.0
+    assert np.all(oracle.index_scores(qpos, w, kneg, 3, 1) == 0.0)
+
+
+# ---------------------------------------------------------------- O4 top-k
+
+def _rank_select(S, k):
+    """Independent characterisation: s is kept iff fewer than k keys beat it,
+    where s' beats s when S[s'] > S[s], or S[s'] == S[s] and s' < s."""
+    n = len(S)
+    keep = [s for s in range(n)
+            if sum(1 for u in range(n) if S[u] > S[s] or (S[u] == S[s] and u < s)) < k]
+    return keep
+
+
+def test_topk_exhaustive_tiny_with_ties():
+    rng = np.random.default_rng(3)
+    for trial in range(60):
+        n = int(rng.integers(1, 13))
+        S = rng.integers(-3, 4, size=n).astype(np.float64)   # heavy ties
+        for k in range(1, n + 3):
+            got = oracle.topk_row(S, k)
+            want = _rank_select(S, k)
+            assert list(got[:len(want)]) == want
+            assert np.all(got[len(want):] == -1) and got.size == k
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(4)
+    T, Lk = 2, 300
+    q = _codes(rng, (T, 16, 128))
+    k = _codes(rng, (Lk, 128))
+    w = rng.standard_normal((T, 16)).astype(np.float32)
+    S = oracle.index_scores(q, w, k, Lk, T)
+    base = oracle.topk(S, Lk, T, 50)
+    for j in (-3, 5):
+        S2 = oracle.index_scores(q, (w * np.float32(2.0 ** j)).astype(np.float32), k, Lk, T)
+        assert np.array_equal(oracle.topk(S2, Lk, T, 50), base)
+    full = oracle.topk(S, Lk, T, 400)
+    for t in range(T):
+        nv = Lk - T + t + 1
+        assert np.array_equal(full[t, :nv], np.arange(nv)) and np.all(full[t, nv:] == -1)
+    # duplicated keys: the lower index wins the last slot
+    S3 = np.array([5.0, 1.0, 3.0, 3.0, 0.0])
+    assert list(oracle.topk_row(S3, 2)) == [0, 2]
+
+
+def test_topk_matches_argpartition_route():
+    rng = np.random.default_rng(5)
+    S = np.round(rng.standard_normal(5000) * 4) / 4           # many ties
+    for k in (1, 17, 2048, 4999, 5000):
+        part = np.argpartition(-S, k - 1)[:k] if k < S.size else np.arange(S.size)
+        kth = S[part].min()
+        above = np.flatnonzero(S > kth)
+        eq = np.flatnonzero(S == kth)[: k - above.size]
+        want = np.sort(np.concatenate([above, eq]))
+        assert np.array_equal(oracle.topk_row(S, k)[:want.size], want)
+
+
+# ------------------------------------------------------ O5 sparse attention
+
+def _sdpa_ref(q, K, V, Hkv, sink, sm_scale, mask):
+    """Library route: torch SDPA in float64 with an explicit boolean mask; a
+    sink becomes an extra key with logit sink[h] and a zero value vector."""
+    T = q.shape[0]
+    grp = 64 // Hkv
+    Kr = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(grp, 0)   # [64,L,192]
+    Vr = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(grp, 0)
+    Q = torch.from_numpy(q).permute(1, 0, 2)                              # [64,T,192]
+    M = torch.from_numpy(mask)[None].expand(64, -1, -1)
+    if sink is not None:
+        # augmented head dim: q' = [q, 1], k' = [k, 0], k_sink = [0, sink/scale]
+        L = Kr.shape[1]
+        Qa = torch.cat([Q, torch.ones(64, T, 1, dtype=Q.dtype)], -1)
+        Ka = torch.cat([Kr, torch.zeros(64, L, 1, dtype=Q.dtype)], -1)
+        ks = torch.zeros(64, 1, Ka.shape[-1], dtype=Q.dtype)
+        ks[:, 0, -1] = torch.from_numpy(np.asarray(sink, dtype=np.float64)) / sm_scale
+        Ka = torch.cat([Ka, ks], 1)
+        Va = torch.cat([Vr, torch.zeros(64, 1, 128, dtype=Q.dtype)], 1)
+        Ma = torch.cat([M, torch.ones(64, T, 1, dtype=torch.bool)], -1)
+        o = F.scaled_dot_product_attention(Qa, Ka, Va, attn_mask=Ma, scale=sm_scale)
+    else:
+        o = F.scaled_dot_product_attention(Q, Kr, Vr, attn_mask=M, scale=sm_scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def _bf16(rng, shape):
+    return synth.encode_bf16(rng.standard_normal(shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("use_sink", [False, True])
+@pytest.mark.parametrize("Hkv", [4, 8])
+def test_attention_full_set_equals_dense_causal(use_sink, Hkv):
+    rng = np.random.default_rng(6)
+    T, Lk = 3, 37
+    q, K, V = _bf16(rng, (T, 64, 192)), _bf16(rng, (Lk, Hkv, 192)), _bf16(rng, (Lk, Hkv, 128))
+    sink = rng.standard_normal(64).astype(np.float32) if use_sink else None
+    sc = float(np.float32(1 / math.sqrt(192)))
+    idx = oracle.topk(np.zeros((T, Lk)), Lk, T, 64)             # k >= n_vis: every visible key
+    got, _ = oracle.sparse_attention(q, K, V, idx, sink, sc)
+    pos = oracle.query_positions(Lk, T)
+    mask = np.arange(Lk)[None, :] <= pos[:, None]
+    ref = _sdpa_ref(oracle.decode_bf16(q), oracle.decode_bf16(K), oracle.decode_bf16(V), Hkv,
+                    sink, sc, mask)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_sink_closed_forms():
+    rng = np.random.default_rng(7)
+    Lk = 20
+    q, K, V = _bf16(rng, (1, 64, 192)), _bf16(rng, (Lk, 4, 192)), _bf16(rng, (Lk, 4, 128))
+    idx = np.array([[1, 4, 9, 13, 19, -1]])
+    sc = 0.07
+    o0, lse0 = oracle.sparse_attention(q, K, V, idx, None, sc)
+    sig = rng.standard_normal(64)
+    o1, lse1 = oracle.sparse_attention(q, K, V, idx, sig, sc)
+    Z0 = np.exp(lse0)
+    assert np.allclose(o1, o0 * (Z0 / (Z0 + np.exp(sig)))[0][:, None], rtol=1e-12, atol=1e-15)
+    assert np.allclose(lse1, np.log(np.exp(lse0) + np.exp(sig)), rtol=1e-12)
+    olo, _ = oracle.sparse_attention(q, K, V, idx, np.full(64, -800.0), sc)
+    assert np.allclose(olo, o0, rtol=1e-13, atol=0)
+    ohi, _ = oracle.sparse_attention(q, K, V, idx, np.full(64, 800.0), sc)
+    assert np.all(np.abs(ohi) < 1e-300)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(8)
+    Lk = 16
+    q, K, V = _bf16(rng, (1, 64, 192)), _bf16(rng, (Lk, 4, 192)), _bf16(rng, (Lk, 4, 128))
+    sig = rng.standard_normal(64)
+    sc = 0.05
+    # one key: o = V e^z / (e^z + e^sigma)
+    o, _ = oracle.sparse_attention(q, K, V, np.array([[6, -1, -1]]), sig, sc)
+    qd, Kd, Vd = oracle.decode_bf16(q)[0], oracle.decode_bf16(K), oracle.decode_bf16(V)
+    for h in (0, 15, 16, 63):
+        z = sc * float(Kd[6, h // 16] @ qd[h])
+        want = Vd[6, h // 16] * (1.0 / (1.0 + math.exp(sig[h] - z)))
+        assert np.allclose(o[0, h], want, rtol=1e-12)
+    # identical V rows: o = v * Z0 / (Z0 + e^sigma)
+    V2 = V.copy()
+    V2[:] = V[3]
+    idx = np.array([[0, 2, 5, 7, 11]])
+    o2, lse2 = oracle.sparse_attention(q, K, V2, idx, sig, sc)
+    _, lse_n = oracle.sparse_attention(q, K, V2, idx, None, sc)
+    frac = np.exp(lse_n - lse2)
+    assert np.allclose(o2[0], (Vd[3][np.arange(64) // 16] * frac[0][:, None]), rtol=1e-12)
+    # permuting the index list leaves the output unchanged
+    o3, _ = oracle.sparse_attention(q, K, V, np.array([[11, 0, 7, 2, 5]]), sig, sc)
+    o4, _ = oracle.sparse_attention(q, K, V, idx, sig, sc)
+    assert np.allclose(o3, o4, rtol=1e-15, atol=1e-15)
+    # empty set: o = 0, lse = sink (or -inf)
+    o5, l5 = oracle.sparse_attention(q, K, V, np.array([[-1, -1]]), sig, sc)
+    assert np.all(o5 == 0) and np.allclose(l5[0], sig)
+    _, l6 = oracle.sparse_attention(q, K, V, np.array([[-1]]), None, sc)
+    assert np.all(np.isneginf(l6))
+
+
+def test_attention_mha_reduction():
+    # with 64 KV heads GQA is plain multi-head attention
+    rng = np.random.default_rng(9)
+    Lk = 10
+    q, K, V = _bf16(rng, (1, 64, 192)), _bf16(rng, (Lk, 64, 192)), _bf16(rng, (Lk, 64, 128))
+    idx = np.array([[0, 3, 4, 9]])
+    got, _ = oracle.sparse_attention(q, K, V, idx, None, 0.1)
+    mask = np.zeros((1, Lk), dtype=bool)
+    mask[0, [0, 3, 4, 9]] = True
+    ref = _sdpa_ref(oracle.decode_bf16(q), oracle.decode_bf16(K), oracle.decode_bf16(V), 64, None, 0.1, mask)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ O6 SWA
+
+@pytest.mark.parametrize("use_sink", [False, True])
+def test_swa_equals_window_masked_dense(use_sink):
+    rng = np.random.default_rng(10)
+    window = 8
+    for n in (1, 5, 8, 9, 30):
+        q, K, V = _bf16(rng, (1, 64, 192)), _bf16(rng, (n, 8, 192)), _bf16(rng, (n, 8, 128))
+        sink = rng.standard_normal(64).astype(np.float32) if use_sink else None
+        last = min(n, window)
+        got, _ = oracle.swa_attention(q, [K[n - last:]], [V[n - last:]], np.array([n]), window, sink, 0.08)
+        p = n - 1
+        mask = np.array([[(p - s) < window and s <= p for s in range(n)]])
+        ref = _sdpa_ref(oracle.decode_bf16(q), oracle.decode_bf16(K), oracle.decode_bf16(V), 8, sink, 0.08, mask)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+        if n <= window:   # short sequence: plain causal attention over everything
+            full, _ = oracle.sparse_attention(q, K, V, np.arange(n)[None], sink, 0.08)
+            assert np.allclose(got, full, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- numbers printed on pages
+
+def test_key_read_accounting_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "pages_constants.json")))
+    L = g["max_position_embeddings"]
+    sparse = oracle.backbone_keys_per_token(L, g["swa_layers"], g["dsa_layers"], g["sliding_window"], g["index_top_k"])
+    dense = oracle.backbone_keys_per_token(L, g["swa_layers"], g["dsa_layers"], g["sliding_window"], g["index_top_k"], dense=True)
+    assert sparse == g["keys_per_token_all_sparse_at_1m"]
+    assert dense == g["keys_per_token_dense_dsa_at_1m"]
+    assert round(dense / sparse) == g["dense_over_sparse_ratio_rounded"]
+    assert g["swa_layers"] + g["dsa_layers"] == g["num_hidden_layers"] == 48
+    assert len(g["dsa_layer_positions"]) == g["dsa_layers"]
+    # the selection constants the library is built around
+    assert (g["index_n_heads"], g["head_dim"], g["v_head_dim"], g["dsa_kv_heads"], g["swa_kv_heads"]) == \
+        (oracle.IDX_HEADS, oracle.QK_DIM, oracle.V_DIM, 4, 8)
+
+
+# ------------------------------------------------------- acceptance helpers
+
+def test_topk_check_detects_far_swap():
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal(1000)
+    ref = oracle.topk_row(S, 100)
+    ok, _ = oracle.topk_check(ref, ref, S, 100)
+    assert ok
+    bad = ref.copy()
+    worst = int(np.argmin(S))
+    bad[np.argmax(S[ref])] = worst            # swap the best key for the worst one
+    bad = np.sort(bad)
+    assert not oracle.topk_check(bad, ref, S, 100)[0]
+    assert not oracle.topk_check(ref[::-1].copy(), ref, S, 100)[0]   # not ascending
+
+
+def test_generator_is_deterministic():
+    a = synth.index_inputs(300, 2, seed=77, plant_frac=0.05)
+    b = synth.index_inputs(300, 2, seed=77, plant_frac=0.05)
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+    c = synth.index_inputs(300, 2, seed=78, plant_frac=0.05)
+    assert not np.array_equal(a["k_idx"], c["k_idx"])
+    assert not np.any((a["k_idx"] & 0x7F) == 0x7F)          # no NaN codes
+
+
+def test_planted_keys_reach_the_top():
+    cfg = synth.DecodeConfig("t", L=4096, T=1, plant_frac=0.01, seed=5)
+    d = synth.index_inputs(cfg.L, cfg.T, cfg.seed, cfg.plant_frac)
+    S = oracle.index_scores(d["q_idx"], d["w"], d["k_idx"], cfg.Lk, 1)[0]
+    top = oracle.topk_row(S, 41)
+    assert np.isin(d["plant_pos"], top).mean() > 0.9
+
+
+# ----------------------------------------- planted mistakes must be caught
+
+def _mutant_scores_relu_after_weight(q, w, k, Lk, T):
+    out = np.full((T, Lk), -np.inf)
+    for t in range(T):
+        n = Lk - T + t + 1
+        lg = oracle.index_logits(q[t:t + 1], k[:n])[0]
+        out[t, :n] = np.maximum(np.asarray(w[t], np.float64) @ lg, 0)
+    return out
+
+
+_REAL_INDEX_SCORES = oracle.index_scores
+
+
+def _mutant_scores_off_by_one_mask(q, w, k, Lk, T):
+    out = _REAL_INDEX_SCORES(q, w, k, Lk, T)
+    out[:, -1] = -np.inf
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_mutant_scores_relu_after_weight, _mutant_scores_off_by_one_mask])
+def test_brute_force_pin_catches_score_mutants(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "index_scores", mutant)
+    with pytest.raises(AssertionError):
+        test_index_scores_brute_force_with_causal_mask()
+
+
+def test_sdpa_pin_catches_gqa_map_mutant(monkeypatch):
+    real = oracle.sparse_attention
+
+    def mutant(q, K, V, idx, sink, sc):
+        # wrong head -> KV-head map: h % Hkv instead of h // (64 / Hkv)
+        perm = np.argsort(np.arange(64) % K.shape[1], kind="stable")
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(64)
+        o, l = real(q[:, inv], K, V, idx, None if sink is None else sink[inv], sc)
+        return o[:, perm], l[:, perm]
+
+    monkeypatch.setattr(oracle, "sparse_attention", mutant)
+    with pytest.raises(AssertionError):
+        test_attention_full_set_equals_dense_causal(False, 4)
+
+
+def test_sink_pin_catches_scaled_sink_mutant(monkeypatch):
+    real = oracle.attend
+
+    def mutant(q, K, V, sink, sc):
+        return real(q, K, V, None if sink is None else sink * sc, sc)
+
+    monkeypatch.setattr(oracle.dsa_oracle, "attend", mutant)
+    with pytest.raises(AssertionError):
+        test_attention_full_set_equals_dense_causal(True, 4)
