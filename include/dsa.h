@@ -1,0 +1,223 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: the single-GPU hot path of a DeepSeek-Sparse-
+ * Attention (DSA) layer and of a sliding-window (SWA) layer, built for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Citation keys (web pages about the Naive-N0.5-Flash release):
+ *   [NoFA]   "Naive-N0.5-Flash: no full-attention layers, and a runtime built
+ *            by AI" (ai.thesatyajit.com) -- property table; section "What 'no
+ *            full-attention layers' means"; section "Inside a DSA layer: the
+ *            lightning indexer" and its Figure 1; section "How much of this
+ *            did AI actually build?".
+ *   [Master] "Naive-N0.5-Flash: the open-weight 309B MoE with no full-attention
+ *            layers at all aims for 2,000 tokens/s per user" (ai-master.dev),
+ *            section "Zero full-attention: what it really changes".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless a
+ *   parameter says otherwise.  `stream` is a hipStream_t passed as void*; NULL
+ *   means the default stream.  Every call only enqueues work on `stream` and
+ *   returns without synchronising; outputs are ready when the stream reaches
+ *   that point.
+ * - Ownership: the caller owns every buffer.  The library never allocates or
+ *   frees memory on a call path and keeps no global mutable state.  Scratch
+ *   space is the caller's workspace `ws` of at least dsa_workspace_bytes()
+ *   bytes (see the workspace contract below).
+ * - Layouts are dense, row-major, C order, with the shapes given per call.
+ *   fp8 values are OCP E4M3FN bytes; bf16 values are raw 16-bit patterns.
+ * - Alignment: every pointer must be 16-byte aligned (torch gives 256 B).
+ * - Query positions: T query tokens are the LAST T of Lk cached tokens, so
+ *   query t (0 <= t < T) sits at position p_t = Lk - T + t and sees keys
+ *   [0, p_t] (causal, including itself; [NoFA] Figure 1 "index sweep over all
+ *   visible keys").
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   on a validation failure nothing is launched and outputs are untouched.  A
+ *   failed launch returns DSA_ERR_HIP.  Faults inside kernels surface at the
+ *   caller's next synchronisation.  No C++ exception crosses the ABI.
+ * - Outputs are fully overwritten (never accumulated).  Results are bitwise
+ *   deterministic: the same inputs give the same bits on every run.
+ *
+ * Workspace contract
+ * ------------------
+ * Calls that take `ws` use it for histograms, per-block candidate lists,
+ * split-softmax partials and completion counters.  A fresh workspace must be
+ * prepared ONCE with dsa_workspace_init() (it zero-fills the counter region
+ * on `stream`); every call leaves the counter region zeroed again when its
+ * work completes, so a workspace can be reused by any sequence of calls on one
+ * stream.  Calls that overlap in time (e.g. on two streams) need separate
+ * workspaces.  If a call's kernels fault, re-initialise the workspace.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed model constants ([NoFA] property table: index_n_heads, the single
+ * fp8 index-key head, num_attention_heads, head_dim / v head dim,
+ * num_key_value_heads (DSA) and swa_num_key_value_heads, index_top_k,
+ * sliding_window). */
+#define DSA_IDX_HEADS 16
+#define DSA_IDX_DIM 128
+#define DSA_Q_HEADS 64
+#define DSA_QK_DIM 192
+#define DSA_V_DIM 128
+#define DSA_KV_HEADS 4
+#define SWA_KV_HEADS 8
+#define DSA_TOPK_MAX 2048
+#define SWA_WINDOW_DEFAULT 128
+#define SWA_WINDOW_MAX 2048
+#define DSA_DECODE_T_MAX 8
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  DSA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
+  DSA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement   */
+  DSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+  DSA_ERR_WORKSPACE = 5,   /* ws is NULL or smaller than dsa_workspace_bytes  */
+  DSA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+} dsa_status;
+
+typedef enum dsa_op {
+  DSA_OP_INDEX_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_ATTN = 2,
+  DSA_OP_SWA_ATTN = 3,
+  DSA_OP_DECODE_STEP = 4
+} dsa_op;
+
+/*
+ * dsa_index_scores -- lightning-indexer scores ([NoFA] "Inside a DSA layer":
+ * 16 fp8 query heads against one shared fp8 key head, ReLU of the dot
+ * product, combined into one score per key by per-head weights):
+ *
+ *   S[t,s] = sum_{h<16} w[t,h] * max( sum_{d<128} q_idx[t,h,d] * k_idx[s,d], 0 )
+ *            for s <= p_t,   S[t,s] = -inf for p_t < s < Lk.
+ *
+ *   q_idx   [T][16][128] fp8 e4m3   (2 KiB per query token)
+ *   w       [T][16] float32
+ *   k_idx   [Lk][128] fp8 e4m3      (key s at byte offset 128*s)
+ *   scores  [T][ld_scores] float32, ld_scores >= Lk; columns >= Lk untouched.
+ *
+ * fp8 products are exact; the 128-term dots and the head sum accumulate in
+ * float32.  T <= 8 uses a streaming scan (decode); larger T uses an fp8 MFMA
+ * contraction (prefill).  Limits: 1 <= T <= Lk < 2^31.
+ */
+dsa_status dsa_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                            int64_t Lk, int32_t T, float* scores, int64_t ld_scores,
+                            void* stream);
+
+/*
+ * dsa_topk -- per query row, the min(k, p_t + 1) visible keys with the
+ * largest scores, ties broken towards the lower key index ([NoFA] "What 'no
+ * full-attention layers' means": first index_top_k entries of a descending
+ * argsort; "How much of this did AI actually build?": stable ties).
+ *
+ *   scores  [T][ld_scores] float32; only columns [0, p_t] of row t are read.
+ *   idx     [T][k] int32 output: the kept key indices in ASCENDING order,
+ *           padded with -1 when p_t + 1 < k.
+ *
+ * -0.0 and +0.0 compare equal.  NaN scores are outside the contract.
+ * Limits: 1 <= k <= 2048, 1 <= T <= Lk < 2^31.  Needs ws (DSA_OP_TOPK).
+ */
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, int64_t Lk, int32_t T, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_gqa_attn -- gathered GQA-4 attention with an optional sink
+ * ([NoFA] "Inside a DSA layer": the main heads attend only to the selected
+ * keys, everything else masked before the softmax; GQA with 4 KV heads on DSA
+ * layers; a sink column per head.  [Master]: sink bias on both attention
+ * types).  For query token t, head h < 64, KV head g = h / 16:
+ *
+ *   z_j    = sm_scale * <q[t,h,:], k_cache[j,g,:]>      for every j in idx[t]
+ *   out    = sum_j e^{z_j} v_cache[j,g,:] / (sum_j e^{z_j} + e^{sink[h]})
+ *   lse    = ln(sum_j e^{z_j} + e^{sink[h]})
+ *
+ * (the sink terms vanish when sink == NULL; the sink is NOT multiplied by
+ * sm_scale).
+ *
+ *   q        [T][64][192] bf16
+ *   k_cache  [Lk][4][192] bf16,  v_cache [Lk][4][128] bf16
+ *   idx      [T][k] int32; entries outside [0, Lk) (e.g. -1 padding) are empty
+ *            slots and are skipped.  Entries must be distinct within a row;
+ *            causality is the caller's business (idx from dsa_topk is causal).
+ *   sink     [64] float32 or NULL
+ *   out      [T][64][128] bf16 (fp32 accumulation, round-to-nearest-even)
+ *   lse      [T][64] float32 or NULL (natural log; -inf for an empty row
+ *            without sink)
+ *
+ * An empty row gives out = 0.  Limits: 1 <= k <= 2048, 1 <= T, Lk < 2^31.
+ * Needs ws (DSA_OP_SPARSE_ATTN).
+ */
+dsa_status sparse_gqa_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           int64_t Lk, const int32_t* idx, int32_t T, int32_t k,
+                           const float* sink, float sm_scale, uint16_t* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * swa_attn -- single-token sliding-window decode for a ragged batch, GQA-8
+ * ([NoFA] "What 'no full-attention layers' means": the SWA path keeps keys
+ * whose offset from the query is below sliding_window = 128, the query itself
+ * included).  Sequence b has seq_len[b] = n_b >= 1 tokens stored at rows
+ * [seq_start[b], seq_start[b] + n_b) of the ragged caches; its query is the
+ * token at position n_b - 1 and attends to positions
+ * [max(0, n_b - window), n_b - 1].  Head h uses KV head h / 8.  The formula is
+ * the one of sparse_gqa_attn over that index set.
+ *
+ *   q          [B][64][192] bf16
+ *   k_cache    [n_rows][8][192] bf16,  v_cache [n_rows][8][128] bf16
+ *   seq_start  [B] int64 (device),  seq_len [B] int32 (device)
+ *   sink       [64] float32 or NULL
+ *   out        [B][64][128] bf16,  lse [B][64] float32 or NULL
+ *
+ * Rows outside [0, n_rows) are never read: a window row outside the cache is
+ * skipped (a sequence with n_b <= 0 is empty).  Limits: 1 <= B,
+ * 1 <= window <= 2048.  Needs ws (DSA_OP_SWA_ATTN).
+ */
+dsa_status swa_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                    int64_t n_rows, const int64_t* seq_start, const int32_t* seq_len, int32_t B,
+                    int32_t window, const float* sink, float sm_scale, uint16_t* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode_step -- one DSA decode (or speculative-verify) step, fused:
+ * index scores -> top-k -> sparse GQA-4 attention, with no host round trip
+ * ([NoFA] Figure 1, the order of one DSA module).  Arguments are those of the
+ * three calls above; idx_out ([T][k] int32) optionally receives the selected
+ * set; scores_out ([T][ld_scores] float32) optionally receives the scores.
+ * Limits: 1 <= T <= 8, 1 <= k <= 2048.  Needs ws (DSA_OP_DECODE_STEP).
+ */
+dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                           const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                           int64_t Lk, int32_t T, int32_t k, const float* sink, float sm_scale,
+                           uint16_t* out, float* lse, int32_t* idx_out,
+                           float* scores_out, int64_t ld_scores,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by `op` for the given sizes (B is the SWA batch; the
+ * other sizes are ignored where they do not apply).  Returns 0 for an invalid
+ * request.  Sizes are upper bounds: a workspace sized for (Lk, T, k, B) serves
+ * every call with smaller sizes of the same op. */
+size_t dsa_workspace_bytes(dsa_op op, int64_t Lk, int32_t T, int32_t k, int32_t B);
+
+/* Prepare a fresh workspace (zero-fills its counter region) on `stream`. */
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* dsa_status_string(dsa_status s);
+
+/* Library version string, e.g. "dsa-mi355x 0.1.0 gfx950". */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

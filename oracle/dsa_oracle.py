@@ -276,9 +276,12 @@ def score_error_bound(q_idx: np.ndarray, w: np.ndarray, k_idx: np.ndarray,
 
 
 def topk_check(gpu_idx_row: np.ndarray, ref_idx_row: np.ndarray,
-               scores_vis: np.ndarray, k: int, rel_gap: float = 1e-4):
+               scores_vis: np.ndarray, k: int, rel_gap: float = 1e-4, err_bound=None):
     """Top-k acceptance: sets equal except inside the near-tie band around the
-    oracle's k-th score.  Returns (ok, message)."""
+    oracle's k-th score.  The band is rel_gap * |tau|; when the per-key score
+    error bound of the GPU arithmetic is given (err_bound[s]), a key may also
+    swap when |S_s - tau| <= err_bound[s] + err_bound[tau key].
+    Returns (ok, message)."""
     n = scores_vis.shape[0]
     g = np.asarray(gpu_idx_row, dtype=np.int64)
     r = np.asarray(ref_idx_row, dtype=np.int64)
@@ -298,9 +301,12 @@ def topk_check(gpu_idx_row: np.ndarray, ref_idx_row: np.ndarray,
         return True, "empty"
     tau = scores_vis[rs].min()
     smax = np.abs(scores_vis).max()
-    band = rel_gap * max(abs(tau), 1e-6 * smax)
+    band = np.full(n, rel_gap * max(abs(tau), 1e-6 * smax))
+    if err_bound is not None:
+        tau_key = rs[np.argmin(scores_vis[rs])]
+        band = np.maximum(band, err_bound[:n] + err_bound[tau_key])
     diff = np.setxor1d(gs, rs)
-    bad = diff[np.abs(scores_vis[diff] - tau) > band]
+    bad = diff[np.abs(scores_vis[diff] - tau) > band[diff]]
     if bad.size:
         return False, f"{bad.size} disagreements outside the near-tie band"
     return True, f"{diff.size // 2} swaps inside the near-tie band"

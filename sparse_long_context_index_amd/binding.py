@@ -1,0 +1,182 @@
+"""ctypes binding of libdsa.so (argument marshalling only).
+
+Every function here forwards device pointers, sizes and the current torch
+stream to the C ABI declared in include/dsa.h; all arithmetic runs in the HIP
+kernels.  There is no fallback: if the library is missing, or a tensor is not
+on a GPU, the call raises.
+
+Functions carry the C names: dsa_index_scores, dsa_topk, sparse_gqa_attn,
+swa_attn, dsa_decode_step, plus the workspace helpers.  Tensors are torch
+tensors on the GPU with the layouts of dsa.h (uint8 for fp8 bytes, bfloat16
+or int16/uint16 for bf16, float32, int32, int64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK = 0
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
+          4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP = range(5)
+
+IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
+DSA_KV_HEADS, SWA_KV_HEADS, TOPK_MAX, DECODE_T_MAX = 4, 8, 2048, 8
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "dsa_index_scores": ([_P, _P, _P, _I64, _I32, _P, _I64, _P], _I32),
+    "dsa_topk": ([_P, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "sparse_gqa_attn": ([_P, _P, _P, _I64, _P, _I32, _I32, _P, _F, _P, _P, _P, _SZ, _P], _I32),
+    "swa_attn": ([_P, _P, _P, _I64, _P, _P, _I32, _I32, _P, _F, _P, _P, _P, _SZ, _P], _I32),
+    "dsa_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _P, _F, _P, _P, _P, _P, _I64,
+                         _P, _SZ, _P], _I32),
+    "dsa_workspace_bytes": ([_I32, _I64, _I32, _I32, _I32], _SZ),
+    "dsa_workspace_init": ([_P, _SZ, _P], _I32),
+    "dsa_status_string": ([_I32], ctypes.c_char_p),
+    "dsa_version": ([], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class DsaError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load libdsa.so (built by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise DsaError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != DSA_OK:
+        msg = load().dsa_status_string(status).decode()
+        raise DsaError(f"{what}: {msg}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise DsaError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise DsaError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(op: int, Lk: int = 0, T: int = 0, k: int = 0, B: int = 0) -> int:
+    return int(load().dsa_workspace_bytes(op, Lk, T, k, B))
+
+
+class Workspace:
+    """A device workspace prepared with dsa_workspace_init (grows on demand)."""
+
+    def __init__(self, nbytes: int = 0, device=None):
+        self.device = device or torch.device("cuda", torch.cuda.current_device())
+        self.buf = None
+        if nbytes:
+            self.ensure(nbytes)
+
+    def ensure(self, nbytes: int):
+        """Grow to at least nbytes (a size from workspace_bytes); a new buffer
+        is prepared with dsa_workspace_init."""
+        if self.buf is not None and self.buf.numel() >= nbytes:
+            return self
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        _check(load().dsa_workspace_init(_dev(self.buf, "ws"), nbytes, _stream()), "dsa_workspace_init")
+        return self
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+
+def dsa_index_scores(q_idx, w, k_idx, Lk: int, T: int, scores=None, ld: Optional[int] = None):
+    if scores is None:
+        scores = torch.empty((T, Lk), dtype=torch.float32, device=q_idx.device)
+    ld = scores.shape[-1] if ld is None else ld
+    _check(load().dsa_index_scores(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), Lk, T,
+                                   _dev(scores, "scores"), ld, _stream()), "dsa_index_scores")
+    return scores
+
+
+def dsa_topk(scores, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] = None,
+             ld: Optional[int] = None):
+    ld = scores.shape[-1] if ld is None else ld
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    ws = (ws or Workspace(device=scores.device)).ensure(workspace_bytes(OP_TOPK, Lk, T, k))
+    _check(load().dsa_topk(_dev(scores, "scores"), ld, Lk, T, k, _dev(idx, "idx"), ws.ptr, ws.nbytes,
+                           _stream()), "dsa_topk")
+    return idx
+
+
+def sparse_gqa_attn(q, k_cache, v_cache, Lk: int, idx, sink, sm_scale: float, out=None, lse=None,
+                    ws: Optional[Workspace] = None):
+    T, k = idx.shape
+    if out is None:
+        out = torch.empty((T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
+    ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_SPARSE_ATTN, Lk, T, k))
+    _check(load().sparse_gqa_attn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk,
+                                  _dev(idx, "idx"), T, k, _dev(sink, "sink"), float(sm_scale),
+                                  _dev(out, "out"), _dev(lse, "lse"), ws.ptr, ws.nbytes, _stream()),
+           "sparse_gqa_attn")
+    return out
+
+
+def swa_attn(q, k_cache, v_cache, seq_start, seq_len, window: int, sink, sm_scale: float, out=None,
+             lse=None, ws: Optional[Workspace] = None):
+    B = seq_len.shape[0]
+    if out is None:
+        out = torch.empty((B, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
+    ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_SWA_ATTN, B=B))
+    _check(load().swa_attn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           k_cache.shape[0], _dev(seq_start, "seq_start"), _dev(seq_len, "seq_len"), B,
+                           window, _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
+                           ws.ptr, ws.nbytes, _stream()), "swa_attn")
+    return out
+
+
+def dsa_decode_step(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: int, sink,
+                    sm_scale: float, out=None, lse=None, idx_out=None, scores_out=None,
+                    ws: Optional[Workspace] = None):
+    if out is None:
+        out = torch.empty((T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
+    ld = scores_out.shape[-1] if scores_out is not None else 0
+    ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_DECODE_STEP, Lk, T, k))
+    _check(load().dsa_decode_step(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
+                                  _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk, T, k,
+                                  _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
+                                  _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld,
+                                  ws.ptr, ws.nbytes, _stream()), "dsa_decode_step")
+    return out

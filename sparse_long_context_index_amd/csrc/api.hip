@@ -1,0 +1,213 @@
+// api.hip -- the extern "C" entry points of libdsa.so: host-side validation,
+// workspace carving and launch sequencing.  Every check happens before the
+// first launch, so a rejected call enqueues nothing and touches no output.
+#include <cmath>
+
+#include "dsa_common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+namespace {
+
+__global__ void zero_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+constexpr int64_t kMaxLk = (int64_t)1 << 31;
+
+dsa_status check_index_args(const void* q_idx, const void* w, const void* k_idx, int64_t Lk, int32_t T) {
+  if (!q_idx || !w || !k_idx) return DSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx)) return DSA_ERR_ALIGN;
+  if (T < 1 || Lk < T || Lk >= kMaxLk) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+dsa_status check_attn_args(const void* q, const void* k, const void* v, const void* out, const void* sink,
+                           const void* lse, float sm_scale) {
+  if (!q || !k || !v || !out) return DSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_ALIGN;
+  if ((sink && !aligned16(sink)) || (lse && !aligned16(lse))) return DSA_ERR_ALIGN;
+  if (!std::isfinite(sm_scale)) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+struct DecodeLayout {
+  size_t scores, idx, topk, attn, total;
+};
+
+DecodeLayout decode_layout(int64_t Lk, int T, int k) {
+  DecodeLayout d;
+  size_t off = kCounterRegionBytes;
+  d.scores = off;
+  off += align_up((size_t)T * Lk * sizeof(float));
+  d.idx = off;
+  off += align_up((size_t)T * k * sizeof(int32_t));
+  d.topk = off;
+  off += align_up(topk_scratch_bytes(Lk, T, k));
+  d.attn = off;
+  off += align_up(attn_scratch_bytes(T, k, DSA_KV_HEADS));
+  d.total = off;
+  return d;
+}
+
+}  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size or value is out of range";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: request not implemented";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown dsa_status";
+}
+
+const char* dsa_version(void) { return "dsa-mi355x 0.1.0 gfx950"; }
+
+size_t dsa_workspace_bytes(dsa_op op, int64_t Lk, int32_t T, int32_t k, int32_t B) {
+  switch (op) {
+    case DSA_OP_INDEX_SCORES:
+      return 0;
+    case DSA_OP_TOPK:
+      if (T < 1 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
+      return kCounterRegionBytes + align_up(topk_scratch_bytes(Lk, T, k));
+    case DSA_OP_SPARSE_ATTN:
+      if (T < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
+      return kCounterRegionBytes + align_up(attn_scratch_bytes(T, k, DSA_KV_HEADS));
+    case DSA_OP_SWA_ATTN:
+      if (B < 1) return 0;
+      return kCounterRegionBytes + align_up(attn_scratch_bytes(B, SWA_WINDOW_MAX, SWA_KV_HEADS));
+    case DSA_OP_DECODE_STEP:
+      if (T < 1 || T > DSA_DECODE_T_MAX || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
+      return decode_layout(Lk, T, k).total;
+  }
+  return 0;
+}
+
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return DSA_ERR_NULL;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  if (ws_bytes < kCounterRegionBytes) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_zero(ws, kCounterRegionBytes, as_stream(stream)));
+}
+
+dsa_status dsa_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int32_t T,
+                            float* scores, int64_t ld_scores, void* stream) {
+  dsa_status s = check_index_args(q_idx, w, k_idx, Lk, T);
+  if (s != DSA_OK) return s;
+  if (!scores) return DSA_ERR_NULL;
+  if (!aligned16(scores)) return DSA_ERR_ALIGN;
+  if (ld_scores < Lk) return DSA_ERR_SHAPE;
+  return hip_status(launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld_scores, as_stream(stream)));
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, int64_t Lk, int32_t T, int32_t k, int32_t* idx,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!scores || !idx) return DSA_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(idx)) return DSA_ERR_ALIGN;
+  if (T < 1 || Lk < T || Lk >= kMaxLk || ld_scores < Lk || k < 1 || k > DSA_TOPK_MAX) return DSA_ERR_SHAPE;
+  if (!ws || ws_bytes < dsa_workspace_bytes(DSA_OP_TOPK, Lk, T, k, 0)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  char* base = static_cast<char*>(ws);
+  return hip_status(launch_topk(scores, ld_scores, Lk, T, k, idx, base, base + kCounterRegionBytes,
+                                as_stream(stream)));
+}
+
+dsa_status sparse_gqa_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t Lk,
+                           const int32_t* idx, int32_t T, int32_t k, const float* sink, float sm_scale,
+                           uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_attn_args(q, k_cache, v_cache, out, sink, lse, sm_scale);
+  if (s != DSA_OK) return s;
+  if (!idx) return DSA_ERR_NULL;
+  if (!aligned16(idx)) return DSA_ERR_ALIGN;
+  if (T < 1 || k < 1 || k > DSA_TOPK_MAX || Lk < 1 || Lk >= kMaxLk) return DSA_ERR_SHAPE;
+  if (!ws || ws_bytes < dsa_workspace_bytes(DSA_OP_SPARSE_ATTN, Lk, T, k, 0)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.n_rows = Lk;
+  a.idx = idx; a.k_len = k; a.T = T;
+  a.sink = sink; a.sm_scale = sm_scale; a.out = out; a.lse = lse;
+  return hip_status(launch_sparse_attn(a, static_cast<char*>(ws) + kCounterRegionBytes, as_stream(stream)));
+}
+
+dsa_status swa_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_rows,
+                    const int64_t* seq_start, const int32_t* seq_len, int32_t B, int32_t window,
+                    const float* sink, float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  dsa_status s = check_attn_args(q, k_cache, v_cache, out, sink, lse, sm_scale);
+  if (s != DSA_OK) return s;
+  if (!seq_start || !seq_len) return DSA_ERR_NULL;
+  if (!aligned16(seq_start) || !aligned16(seq_len)) return DSA_ERR_ALIGN;
+  if (B < 1 || window < 1 || window > SWA_WINDOW_MAX || n_rows < 1) return DSA_ERR_SHAPE;
+  if (!ws || ws_bytes < dsa_workspace_bytes(DSA_OP_SWA_ATTN, 0, 0, 0, B)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.n_rows = n_rows;
+  a.seq_start = seq_start; a.seq_len = seq_len; a.window = window; a.T = B;
+  a.sink = sink; a.sm_scale = sm_scale; a.out = out; a.lse = lse;
+  return hip_status(launch_swa_attn(a, static_cast<char*>(ws) + kCounterRegionBytes, as_stream(stream)));
+}
+
+dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                           const uint16_t* k_cache, const uint16_t* v_cache, int64_t Lk, int32_t T, int32_t k,
+                           const float* sink, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
+                           float* scores_out, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_index_args(q_idx, w, k_idx, Lk, T);
+  if (s != DSA_OK) return s;
+  s = check_attn_args(q, k_cache, v_cache, out, sink, lse, sm_scale);
+  if (s != DSA_OK) return s;
+  if (T > DSA_DECODE_T_MAX || k < 1 || k > DSA_TOPK_MAX) return DSA_ERR_SHAPE;
+  if ((idx_out && !aligned16(idx_out)) || (scores_out && !aligned16(scores_out))) return DSA_ERR_ALIGN;
+  if (scores_out && ld_scores < Lk) return DSA_ERR_SHAPE;
+  const size_t need = dsa_workspace_bytes(DSA_OP_DECODE_STEP, Lk, T, k, 0);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+
+  const DecodeLayout L = decode_layout(Lk, T, k);
+  char* base = static_cast<char*>(ws);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(base + L.scores);
+  const int64_t ld = scores_out ? ld_scores : Lk;
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+  hipStream_t st = as_stream(stream);
+
+  // up to kScanHistTMax tokens the scan also builds the top-k's level-1 histogram
+  const bool fused = T <= kScanHistTMax && topk_multi_block(Lk, T);
+  hipError_t e = launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld, st, fused ? base : nullptr);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  e = launch_topk(scores, ld, Lk, T, k, idx, base, base + L.topk, st, fused);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  AttnArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.n_rows = Lk;
+  a.idx = idx; a.k_len = k; a.T = T;
+  a.sink = sink; a.sm_scale = sm_scale; a.out = out; a.lse = lse;
+  return hip_status(launch_sparse_attn(a, base + L.attn, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,278 @@
+// index_scores.hip -- lightning-indexer scores on gfx950.
+//
+// S[t,s] = sum_h w[t,h] * max(q_idx[t,h,:] . k_idx[s,:], 0) for s <= p_t, -inf
+// beyond ("Naive-N0.5-Flash: no full-attention layers, and a runtime built by
+// AI", section "Inside a DSA layer: the lightning indexer": 16 fp8 query heads
+// against one shared fp8 key head, ReLU of the dot, per-head weights combine
+// them into one score per key).
+//
+// Both kernels put the 16 index heads on the M dimension of a 16x16 MFMA and
+// 16 keys on N, so one accumulator holds all head logits of 16 keys for one
+// query token: 4 heads of one key per lane.  The ReLU-weighted head sum is 4
+// FMAs in the lane plus two cross-lane-group butterflies.
+//
+//  * idx_scan_kernel<T> (T <= 8, decode / speculative verify): a coalesced
+//    stream over the 128-byte fp8 key rows (2 KiB per 16-key tile, several
+//    tiles in flight per wave).  The stream is HBM-bound, so the dot engine
+//    can afford exactness: fp8 bytes are widened to bf16 in registers
+//    (lossless) and multiplied on the bf16 MFMA, whose products are exact and
+//    whose sums are fp32-accurate.  Optionally the kernel also builds the
+//    level-1 radix histogram of its scores for the top-k that follows.
+//  * idx_gemm_kernel (T > 8, prefill): a [T*16 x 128] x [128 x Lk] contraction
+//    on the fp8 MFMA (16x16x128), tiled 32 tokens x 128 keys per workgroup with
+//    an XCD-aware tile order, causal tiles masked, same epilogue.  The fp8
+//    MFMA adds each group of 8 products after aligning them to the group's
+//    largest exponent, so its sums carry less precision than fp32 (measured
+//    and bounded in the tests).
+#include "dsa_common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kScanUnroll = 4;   // 16-key tiles per wave in flight
+constexpr int kScanBlocks = 512; // target workgroups of the decode scan
+
+__device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
+  // 32 bytes as two 16-byte loads (only 16-byte alignment is guaranteed)
+  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+  i32x4 lo = __builtin_nontemporal_load(q);
+  i32x4 hi = __builtin_nontemporal_load(q + 1);
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ i32x8 load_frag32_cached(const uint8_t* p) {
+  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+  i32x4 lo = q[0];
+  i32x4 hi = q[1];
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// ReLU-weighted head sum for the key of this lane's column.  c holds heads
+// 4*grp + {0..3}; wv the matching weights.  The two butterflies add the
+// partial sums of the four lane groups; every lane ends with the same bits.
+__device__ __forceinline__ float relu_weighted_sum(const f32x4& c, const float* wv) {
+  float s = wv[0] * fmaxf(c[0], 0.0f);
+  s = fmaf(wv[1], fmaxf(c[1], 0.0f), s);
+  s = fmaf(wv[2], fmaxf(c[2], 0.0f), s);
+  s = fmaf(wv[3], fmaxf(c[3], 0.0f), s);
+  s += shfl_xor_f(s, 16);
+  s += shfl_xor_f(s, 32);
+  return s;
+}
+
+// 32 fp8 bytes -> four bf16x8 MFMA operands (k-step s takes bytes 8s..8s+7)
+__device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, false);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, true);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, false);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, true);
+    out[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+}
+
+// with_hist: also build the level-1 radix histogram of the scores (top-k's
+// first digit); this workgroup adds its counts to replica blockIdx.x % 16.
+template <int T>
+__global__ __launch_bounds__(256) void idx_scan_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
+    int64_t ld, int64_t tiles_per_wg, TopkCounters ctr, int with_hist) {
+  extern __shared__ uint32_t lhist[];                // [T][4096] when with_hist
+  __shared__ uint32_t red_sm[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  if (with_hist) {
+    for (int i = threadIdx.x; i < T * kHistBins; i += 256) lhist[i] = 0;
+    __syncthreads();
+  }
+
+  bf16x8 a[T][4];
+  float wv[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    widen_fp8(load_frag32_cached(q_idx + (size_t)(t * 16 + col) * 128 + 32 * grp), a[t]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[t][i] = w[t * 16 + 4 * grp + i];
+  }
+
+  const int64_t ntiles = cdiv(Lk, 16);
+  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
+  const int64_t tile_end = tile0 + tiles_per_wg < ntiles ? tile0 + tiles_per_wg : ntiles;
+  const int64_t last = Lk - 1;
+  constexpr int64_t kStep = 4 * kScanUnroll;        // tiles per workgroup per batch
+
+  auto load_batch = [&](i32x8* kb, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      int64_t key = (base + u * 4 + wave) * 16 + col;
+      key = key < last ? key : last;                 // ragged tail: stay in bounds
+      kb[u] = load_frag32(k_idx + key * 128 + 32 * grp);
+    }
+  };
+  auto score_batch = [&](const i32x8* kb, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int64_t tile = base + u * 4 + wave;
+      if (tile >= tile_end) continue;                // wave-uniform
+      const int64_t key = tile * 16 + col;
+      bf16x8 b[4];
+      widen_fp8(kb[u], b);
+      float s[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) c = mfma_bf16_16x16x32(a[t][k4], b[k4], c);
+        s[t] = relu_weighted_sum(c, wv[t]);
+        if (key > Lk - T + t) s[t] = -INFINITY;       // causal: beyond p_t
+      }
+      if (key < Lk) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          if ((t & 3) == grp) {
+            scores[(int64_t)t * ld + key] = s[t];
+            if (with_hist && key <= Lk - T + t)
+              atomicAdd(&lhist[t * kHistBins + (order_key(s[t]) >> 20)], 1u);
+          }
+      }
+    }
+  };
+
+  // two batches in flight: the next batch's loads are issued before the
+  // current batch is scored
+  i32x8 ka[kScanUnroll], kb2[kScanUnroll];
+  if (tile0 < tile_end) load_batch(ka, tile0);
+  for (int64_t base = tile0; base < tile_end; base += 2 * kStep) {
+    if (base + kStep < tile_end) load_batch(kb2, base + kStep);
+    score_batch(ka, base);
+    if (base + 2 * kStep < tile_end) load_batch(ka, base + 2 * kStep);
+    if (base + kStep < tile_end) score_batch(kb2, base + kStep);
+  }
+  if (with_hist) {
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+      flush_level1<256>(ctr, blockIdx.x % kHistReplicas, t, lhist + t * kHistBins, red_sm);
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- prefill
+constexpr int kGemmTok = 32;     // tokens per workgroup (8 per wave)
+constexpr int kGemmKeys = 128;   // keys per workgroup (8 blocks of 16)
+constexpr int kGemmGroupT = 32;  // token tiles per L2 super-tile
+
+__global__ __launch_bounds__(256) void idx_gemm_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, int64_t Lk, int T, float* __restrict__ scores,
+    int64_t ld, int64_t n_ttiles, int64_t n_ktiles, int64_t per_xcd) {
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
+  // range of logical tiles, ordered so consecutive tiles share a key tile
+  // and a group of token tiles stays resident in that XCD's L2.
+  const int64_t bid = blockIdx.x;
+  const int64_t logical = (bid & 7) * per_xcd + (bid >> 3);
+  const int64_t total = n_ttiles * n_ktiles;
+  if (logical >= total) return;
+  const int64_t gsz = kGemmGroupT * n_ktiles;
+  const int64_t g = logical / gsz;
+  const int64_t rem = logical - g * gsz;
+  const int64_t g_tiles = (g + 1) * kGemmGroupT <= n_ttiles ? kGemmGroupT : n_ttiles - g * kGemmGroupT;
+  const int64_t ktile = rem / g_tiles;
+  const int64_t ttile = g * kGemmGroupT + rem % g_tiles;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int t0 = (int)(ttile * kGemmTok) + wave * 8;
+  const int64_t s0 = ktile * kGemmKeys;
+  if (t0 >= T) return;                                 // wave-uniform
+
+  // this wave's 8 tokens see keys up to p_{t0+7}; skip the MFMAs when every
+  // key of the tile is beyond p_{t0}+... and only write -inf
+  const int64_t pmax = Lk - T + (t0 + 7 < T ? t0 + 7 : T - 1);
+  const bool all_masked = s0 > pmax;
+
+  i32x8 a[8];
+  float wv[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int t = t0 + j < T ? t0 + j : T - 1;
+    if (!all_masked) a[j] = load_frag32_cached(q_idx + (size_t)(t * 16 + col) * 128 + 32 * grp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[j][i] = w[t * 16 + 4 * grp + i];
+  }
+  const int64_t last = Lk - 1;
+#pragma unroll 1
+  for (int kb = 0; kb < kGemmKeys / 16; ++kb) {
+    const int64_t key = s0 + kb * 16 + col;
+    if (s0 + kb * 16 >= Lk) break;                     // wave-uniform
+    float s[8];
+    if (!all_masked) {
+      const int64_t keyc = key < last ? key : last;
+      i32x8 b = load_frag32_cached(k_idx + keyc * 128 + 32 * grp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f32x4 c = mfma_f8_16x16x128(a[j], b, f32x4{0.f, 0.f, 0.f, 0.f});
+        s[j] = relu_weighted_sum(c, wv[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + j;
+      if (all_masked || key > Lk - T + t) s[j] = -INFINITY;
+      if ((j & 3) == grp && t < T && key < Lk) scores[(int64_t)t * ld + key] = s[j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                               int64_t Lk, int T, float* scores, int64_t ld, hipStream_t st,
+                               void* topk_counters) {
+  const int with_hist = topk_counters != nullptr;
+  const TopkCounters ctr = topk_counters ? counters_at(topk_counters) : TopkCounters{};
+  if (T <= kDecodeTMax) {
+    if (with_hist && T > kScanHistTMax) return hipErrorInvalidValue;
+    const int64_t ntiles = cdiv(Lk, 16);
+    const int64_t step = 4 * kScanUnroll;
+    // about kScanBlocks workgroups, each a contiguous range of whole steps
+    const int64_t tpw = cdiv(cdiv(ntiles, kScanBlocks), step) * step;
+    const dim3 grid((unsigned)cdiv(ntiles, tpw));
+    const size_t lds = with_hist ? (size_t)T * kHistBins * sizeof(uint32_t) : 0;
+    switch (T) {
+#define DSA_SCAN_CASE(n) \
+  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, grid, dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, tpw, ctr, with_hist); break;
+      DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
+      DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
+#undef DSA_SCAN_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (with_hist) return hipErrorInvalidValue;
+  const int64_t n_ttiles = cdiv(T, kGemmTok);
+  const int64_t n_ktiles = cdiv(Lk, kGemmKeys);
+  const int64_t per_xcd = cdiv(n_ttiles * n_ktiles, 8);
+  const int64_t nblocks = per_xcd * 8;
+  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(idx_gemm_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, q_idx, w, k_idx,
+                     Lk, T, scores, ld, n_ttiles, n_ktiles, per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,54 @@
+// kernels.hpp -- launchers of the HIP kernels (internal to libdsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kDecodeTMax = 8;            // streaming-scan limit of the indexer
+constexpr int kScanHistTMax = 4;          // the scan also builds the top-k histogram up to here
+constexpr int kTopkMultiRowsMax = 8;      // rows handled by the multi-block top-k
+
+// ---- index scores
+// topk_counters: optional workspace counter region; when given (T <=
+// kScanHistTMax) the scan also builds the top-k's level-1 histogram there
+hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                               int64_t Lk, int T, float* scores, int64_t ld, hipStream_t st,
+                               void* topk_counters = nullptr);
+
+// ---- top-k
+size_t topk_scratch_bytes(int64_t Lk, int T, int k);
+bool topk_multi_block(int64_t Lk, int T);   // few long rows: the multi-block path
+// hist_ready: the level-1 histogram of these scores is already in the counter
+// region (built by the scan); otherwise launch_topk builds it first.
+hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
+                       void* ws_counters, void* scratch, hipStream_t st, bool hist_ready = false);
+
+// ---- gathered attention
+struct AttnArgs {
+  const uint16_t* q;       // [units_t][64][192]
+  const uint16_t* k;       // [rows][Hkv][192]
+  const uint16_t* v;       // [rows][Hkv][128]
+  int64_t n_rows;          // rows of k / v
+  // index source: explicit list (idx != nullptr) or a window per sequence
+  const int32_t* idx;      // [T][k]
+  int k_len;               // entries per idx row
+  const int64_t* seq_start;  // [B]
+  const int32_t* seq_len;    // [B]
+  int window;
+  int T;                   // query tokens (DSA) or sequences (SWA)
+  const float* sink;       // [64] or null
+  float sm_scale;
+  uint16_t* out;           // [T][64][128]
+  float* lse;              // [T][64] or null
+};
+size_t attn_scratch_bytes(int T, int k_len, int hkv);
+hipError_t launch_sparse_attn(const AttnArgs& a, void* scratch, hipStream_t st);
+hipError_t launch_swa_attn(const AttnArgs& a, void* scratch, hipStream_t st);
+
+// ---- workspace
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,519 @@
+// topk.hip -- exact per-row top-k with stable ties on gfx950.
+//
+// Semantics ("Naive-N0.5-Flash: no full-attention layers, and a runtime built
+// by AI", section "What 'no full-attention layers' means": the DSA path keeps
+// the first index_top_k entries of a descending argsort of the index scores;
+// section "How much of this did AI actually build?": the argsort is stable):
+// keep the min(k, n) visible keys ordered by (score desc, index asc) and emit
+// them in ascending index order, padded with -1.
+//
+// Method: radix select on the order-preserving 32-bit key of each score in
+// three digits (bits 31..20, 19..8, 7..0).  The threshold key tau is exact;
+// keys above tau are kept, and of the keys equal to tau the r lowest indices
+// are kept (r = k - #above).  Candidates are gathered in index order, so the
+// emission is an ordered compaction -- no sort is needed and the result does
+// not depend on scheduling.
+//
+//  * Few long rows (decode, T <= 16): many workgroups per row.
+//      topk_hist_kernel     level-1 histogram (LDS, then global atomics)
+//      topk_collect_kernel  each block finds the level-1 threshold digit,
+//                           compacts its candidates (digit >= threshold) in
+//                           order into its own slot, adds level-2 digits of
+//                           the boundary bin to a global histogram; the last
+//                           block of the row resolves tau and emits the row.
+//  * Many rows (prefill): topk_row_kernel, one 1024-thread workgroup per row,
+//    candidates in LDS.
+// A candidate slot that overflows switches the row's final pass to reading
+// the scores row itself (same result, slower).
+#include "dsa_common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kCollectThreads = 256;
+constexpr int kCollectPer = 16;                                 // per thread
+constexpr int kCollectRange = kCollectThreads * kCollectPer;    // per block
+constexpr int kSlotCap = 512;                                   // candidates per block
+constexpr int kMaxSegs = 1024;                                  // blocks per row (multi-block path)
+constexpr int kCandCap = 6144;                                  // LDS candidates of the final block
+constexpr int kHistRange = 2048;                                // per hist block
+constexpr int kRowThreads = 1024;
+constexpr int kRowCap = 6144;                                   // LDS candidates per row
+
+// ------------------------------------------------------------ block helpers
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sm[wv] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    uint32_t s = sm[i];
+    base += (i < wv) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Largest bin b with suffix(b) = sum_{b' >= b} hist[b'] >= need (need >= 1 and
+// the histogram total >= need).  Writes the bin and suffix(b + 1) to *bin and
+// *above (shared).  All threads must call it.
+template <int NT, int NB>
+__device__ void find_threshold_bin(const uint32_t* hist, uint32_t need, uint32_t* scan_sm,
+                                   uint32_t* bin, uint32_t* above) {
+  constexpr int PER = NB >= NT ? NB / NT : 1;
+  static_assert(NB < NT || PER * NT == NB, "bins per thread");
+  const int j = threadIdx.x;
+  const int base = NB - (j + 1) * PER;          // thread 0 owns the top bins
+  const bool owns = base >= 0;                  // threads beyond the bins own none
+  uint32_t h[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    h[i] = owns ? hist[base + i] : 0u;
+    sum += h[i];
+  }
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan<NT>(sum, scan_sm, &tot);
+  if (owns && excl < need && excl + sum >= need) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (acc + h[i] >= need) {
+        *bin = (uint32_t)(base + i);
+        *above = acc;
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Sources of candidates for the final pass, walked in ascending index order
+// as nseg() consecutive segments.  get() returns (key, index); key 0 marks an
+// element that is not a candidate.
+struct SlotSource {      // per-block ordered slots (multi-block path)
+  const uint2* slots;    // [G][kSlotCap] of this row
+  const uint32_t* cnt;   // [G]
+  int G;
+  __device__ int nseg() const { return G; }
+  __device__ int seg_len(int w) const { return (int)cnt[w]; }
+  __device__ uint2 get(int w, int i) const { return slots[(size_t)w * kSlotCap + i]; }
+};
+
+struct RowSource {       // the scores row itself (overflow fallback)
+  const float* row;
+  int64_t n;
+  int64_t seg;           // elements per segment
+  int G;
+  uint32_t b1;           // level-1 digit filter (0 keeps everything)
+  __device__ int nseg() const { return G; }
+  __device__ int seg_len(int w) const {
+    int64_t lo = (int64_t)w * seg;
+    int64_t hi = lo + seg < n ? lo + seg : n;
+    return hi > lo ? (int)(hi - lo) : 0;
+  }
+  __device__ uint2 get(int w, int i) const {
+    int64_t s = (int64_t)w * seg + i;
+    uint32_t key = order_key(row[s]);
+    if ((key >> 20) < b1) key = 0;
+    return make_uint2(key, (uint32_t)s);
+  }
+};
+
+struct FlatSource {      // an ordered candidate array (LDS, row kernel)
+  const uint2* a;
+  int n;
+  int G;                 // segments = threads
+  __device__ int nseg() const { return G; }
+  __device__ int seg_len(int w) const {
+    int per = (n + G - 1) / G;
+    int lo = w * per;
+    int hi = lo + per < n ? lo + per : n;
+    return hi > lo ? hi - lo : 0;
+  }
+  __device__ uint2 get(int w, int i) const { return a[w * ((n + G - 1) / G) + i]; }
+};
+
+struct FinalShared {
+  uint32_t scan[1024 / 64];
+  uint32_t h3[kHist3Bins];
+  uint32_t bin, above;
+};
+
+// Resolve tau from the level-2 histogram (h2, global or shared) and a level-3
+// pass over the candidates, then emit the row.  One workgroup, NT threads.
+//   all_mode: n <= k, every visible key is kept.
+//   k1: keys still to take from the level-1 boundary bin b1.
+template <int NT, class Src>
+__device__ void final_select(const Src& src, int k, bool all_mode, uint32_t b1, uint32_t k1,
+                             const uint32_t* h2, FinalShared& fs, int32_t* out_row) {
+  uint32_t tau = 0, r = 0;
+  if (!all_mode) {
+    find_threshold_bin<NT, kHistBins>(h2, k1, fs.scan, &fs.bin, &fs.above);
+    const uint32_t b2 = fs.bin;
+    const uint32_t k2 = k1 - fs.above;
+    for (int i = threadIdx.x; i < kHist3Bins; i += NT) fs.h3[i] = 0;
+    __syncthreads();
+    const uint32_t pre = (b1 << 12) | b2;          // key bits 31..8 of the boundary
+    const int nseg = src.nseg();
+    for (int w = threadIdx.x; w < nseg; w += NT) {
+      const int len = src.seg_len(w);
+      for (int i = 0; i < len; ++i) {
+        const uint32_t key = src.get(w, i).x;
+        if ((key >> 8) == pre) atomicAdd(&fs.h3[key & 0xFF], 1u);
+      }
+    }
+    __syncthreads();
+    find_threshold_bin<NT, kHist3Bins>(fs.h3, k2, fs.scan, &fs.bin, &fs.above);
+    tau = (pre << 8) | fs.bin;
+    r = k2 - fs.above;
+  }
+  // ordered emission: a thread owns a contiguous run of segments
+  const int nseg = src.nseg();
+  const int spt = (nseg + NT - 1) / NT;
+  const int w0 = threadIdx.x * spt;
+  const int w1 = w0 + spt < nseg ? w0 + spt : nseg;
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int w = w0; w < w1; ++w) {
+    const int len = src.seg_len(w);
+    for (int i = 0; i < len; ++i) {
+      const uint32_t key = src.get(w, i).x;
+      n_gt += key > tau;
+      n_eq += key == tau;
+    }
+  }
+  uint32_t tot_gt, tot_eq;
+  const uint32_t gt_base = block_excl_scan<NT>(n_gt, fs.scan, &tot_gt);
+  const uint32_t eq_base = block_excl_scan<NT>(n_eq, fs.scan, &tot_eq);
+  if (all_mode) r = 0;                       // tau = 0: every candidate is "above"
+  uint32_t pos = gt_base + (eq_base < r ? eq_base : r);
+  uint32_t eq_seen = eq_base;
+  for (int w = w0; w < w1; ++w) {
+    const int len = src.seg_len(w);
+    for (int i = 0; i < len; ++i) {
+      const uint2 e = src.get(w, i);
+      bool take = e.x > tau;
+      if (e.x == tau) {
+        take = eq_seen < r;
+        ++eq_seen;
+      }
+      if (take && pos < (uint32_t)k) out_row[pos++] = (int32_t)e.y;
+    }
+  }
+  const uint32_t total = tot_gt + (tot_eq < r ? tot_eq : r);
+  for (uint32_t i = total + threadIdx.x; i < (uint32_t)k; i += NT) out_row[i] = -1;
+}
+
+// ------------------------------------------------------------ multi-block path
+
+__global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
+                                                        int64_t Lk, int T, TopkCounters ctr) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t red[4];
+  const int t = blockIdx.y;
+  const int64_t n = Lk - T + t + 1;
+  const int64_t lo = (int64_t)blockIdx.x * kHistRange;
+  if (lo >= n) return;                                   // block-uniform
+  const int64_t hi = lo + kHistRange < n ? lo + kHistRange : n;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+  __syncthreads();
+  const float* row = scores + (int64_t)t * ld;
+  for (int64_t s = lo + threadIdx.x; s < hi; s += 256) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
+  __syncthreads();
+  flush_level1<256>(ctr, blockIdx.x % kHistReplicas, t, h, red);
+}
+
+// Level-1 threshold digit: the largest bin whose suffix count reaches `need`,
+// searched downward from the highest non-empty bin in chunks of NT bins (one
+// chunk almost always suffices).
+template <int NT>
+__device__ void find_b1(const TopkCounters& ctr, int t, uint32_t need, uint32_t* scan_sm, uint32_t* s_bin,
+                        uint32_t* s_above) {
+  uint32_t mb = 0;
+#pragma unroll
+  for (int r = 0; r < kHistReplicas; ++r) {
+    const uint32_t v = ctr.maxbin[r * kMaxCounterRows + t];
+    mb = v > mb ? v : mb;
+  }
+  uint32_t acc = 0;
+  for (int c0 = (int)mb - 1; c0 >= 0; c0 -= NT) {
+    const int bin = c0 - (int)threadIdx.x;
+    uint32_t hv[kHistReplicas];
+#pragma unroll
+    for (int r = 0; r < kHistReplicas; ++r) hv[r] = bin >= 0 ? h1_row(ctr, r, t)[bin] : 0u;
+    uint32_t h = 0;
+#pragma unroll
+    for (int r = 0; r < kHistReplicas; ++r) h += hv[r];
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan<NT>(h, scan_sm, &tot);
+    if (acc + excl < need && acc + excl + h >= need) {
+      *s_bin = (uint32_t)bin;
+      *s_above = acc + excl;
+    }
+    acc += tot;
+    if (acc >= need) break;                                            // uniform
+  }
+  __syncthreads();
+}
+
+// Each block compacts, in index order, the keys of its range whose level-1
+// digit reaches the threshold digit into its own slot, and adds the level-2
+// digits of the boundary bin to the row's level-2 histogram.
+__global__ __launch_bounds__(256) void topk_collect_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
+    uint2* __restrict__ slots, uint32_t* __restrict__ slot_cnt, int G) {
+  __shared__ uint32_t h2[kHistBins];
+  __shared__ uint32_t scan_sm[4];
+  __shared__ uint32_t s_b1, s_above1;
+  const int t = blockIdx.y;
+  const int wg = blockIdx.x;
+  const int64_t n = Lk - T + t + 1;
+  const bool all_mode = n <= (int64_t)k;
+  const float* row = scores + (int64_t)t * ld;
+  const int64_t lo = (int64_t)wg * kCollectRange + (int64_t)threadIdx.x * kCollectPer;
+
+  float v[kCollectPer];
+#pragma unroll
+  for (int e = 0; e < kCollectPer; ++e) v[e] = (lo + e < n) ? row[lo + e] : 0.0f;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) h2[i] = 0;
+
+  uint32_t b1 = 0;
+  if (!all_mode) {
+    find_b1<256>(ctr, t, (uint32_t)k, scan_sm, &s_b1, &s_above1);
+    b1 = s_b1;
+  } else {
+    __syncthreads();
+  }
+
+  uint32_t key[kCollectPer];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kCollectPer; ++e) {
+    key[e] = order_key(v[e]);
+    const bool f = (lo + e < n) && (key[e] >> 20) >= b1;
+    cnt += f;
+    if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&h2[(key[e] >> 8) & 0xFFF], 1u);
+  }
+  uint32_t total;
+  uint32_t pos = block_excl_scan<256>(cnt, scan_sm, &total);
+  uint2* my_slots = slots + ((size_t)t * G + wg) * kSlotCap;
+#pragma unroll
+  for (int e = 0; e < kCollectPer; ++e) {
+    const bool f = (lo + e < n) && (key[e] >> 20) >= b1;
+    if (f) {
+      if (pos < kSlotCap) my_slots[pos] = make_uint2(key[e], (uint32_t)(lo + e));
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) {
+    slot_cnt[(size_t)t * G + wg] = total < kSlotCap ? total : kSlotCap;
+    if (total > kSlotCap) atomicOr(&ctr.overflow[t], 1u);
+  }
+  if (!all_mode) {
+    uint32_t* g2 = ctr.h2 + (size_t)t * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      const uint32_t c = h2[i];
+      if (c) atomicAdd(&g2[i], c);
+    }
+  }
+}
+
+constexpr int kFinalThreads = 1024;
+static_assert(kMaxSegs <= kFinalThreads, "one slot count per thread");
+
+struct FinalKernelShared {
+  uint2 cand[kCandCap];
+  uint32_t offs[kMaxSegs + 1];
+  FinalShared fs;
+  uint32_t b1, above1;
+};
+
+// One block per row: gathers the ordered candidates of all slots into LDS
+// (independent loads), resolves the exact threshold and emits the row, then
+// leaves the row's counters zeroed.
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
+    const uint2* __restrict__ slots, const uint32_t* __restrict__ slot_cnt, int G, int32_t* __restrict__ idx) {
+  __shared__ FinalKernelShared sh;
+  const int t = blockIdx.x;
+  const int64_t n = Lk - T + t + 1;
+  const bool all_mode = n <= (int64_t)k;
+  const float* row = scores + (int64_t)t * ld;
+  int32_t* out_row = idx + (size_t)t * k;
+  const uint32_t ovf = ctr.overflow[t];
+  const uint32_t c_own = (int)threadIdx.x < G ? slot_cnt[(size_t)t * G + threadIdx.x] : 0u;
+
+  uint32_t b1 = 0, k1 = 0;
+  if (!all_mode) {
+    find_b1<kFinalThreads>(ctr, t, (uint32_t)k, sh.fs.scan, &sh.b1, &sh.above1);
+    b1 = sh.b1;
+    k1 = (uint32_t)k - sh.above1;
+  }
+  uint32_t M;
+  const uint32_t base = block_excl_scan<kFinalThreads>(c_own, sh.fs.scan, &M);
+  if ((int)threadIdx.x < G) sh.offs[threadIdx.x] = base;
+  if (threadIdx.x == 0) sh.offs[G] = M;
+  __syncthreads();
+  const uint32_t* g2 = ctr.h2 + (size_t)t * kHistBins;
+  if (!ovf && M <= (uint32_t)kCandCap) {
+    const uint2* rs = slots + (size_t)t * G * kSlotCap;
+    for (uint32_t e0 = threadIdx.x; e0 < M; e0 += 8 * kFinalThreads) {
+      uint2 buf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = e0 + j * kFinalThreads;
+        buf[j] = make_uint2(0u, 0u);
+        if (e < M) {
+          int lo_s = 0, hi_s = G - 1;                    // last segment with offs <= e
+          while (lo_s < hi_s) {
+            const int mid = (lo_s + hi_s + 1) >> 1;
+            if (sh.offs[mid] <= e) lo_s = mid; else hi_s = mid - 1;
+          }
+          buf[j] = rs[(size_t)lo_s * kSlotCap + (e - sh.offs[lo_s])];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = e0 + j * kFinalThreads;
+        if (e < M) sh.cand[e] = buf[j];
+      }
+    }
+    __syncthreads();
+    FlatSource src{sh.cand, (int)M, kFinalThreads};
+    final_select<kFinalThreads>(src, k, all_mode, b1, k1, g2, sh.fs, out_row);
+  } else {
+    RowSource src{row, n, kCollectRange, G, all_mode ? 0u : b1};
+    final_select<kFinalThreads>(src, k, all_mode, b1, k1, g2, sh.fs, out_row);
+  }
+  // leave the row's counters zeroed for the next call
+  __syncthreads();
+  for (int r = 0; r < kHistReplicas; ++r) {
+    uint4* z = reinterpret_cast<uint4*>(h1_row(ctr, r, t));
+    for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z[i] = make_uint4(0, 0, 0, 0);
+  }
+  uint4* z2 = reinterpret_cast<uint4*>(ctr.h2 + (size_t)t * kHistBins);
+  for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z2[i] = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x < kHistReplicas) ctr.maxbin[threadIdx.x * kMaxCounterRows + t] = 0;
+  if (threadIdx.x == 0) ctr.overflow[t] = 0;
+}
+
+// ------------------------------------------------------------ row path
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t Lk, int T, int k,
+                                                               int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint2 cand[kRowCap];
+  __shared__ FinalShared fs;
+  __shared__ uint32_t s_b1, s_above1;
+  const int t = blockIdx.x;
+  const int64_t n = Lk - T + t + 1;
+  const bool all_mode = n <= (int64_t)k;
+  const float* row = scores + (int64_t)t * ld;
+  int32_t* out_row = idx + (size_t)t * k;
+
+  uint32_t b1 = 0, k1 = 0;
+  if (!all_mode) {
+    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = threadIdx.x; s < n; s += kRowThreads) atomicAdd(&hist[order_key(row[s]) >> 20], 1u);
+    __syncthreads();
+    find_threshold_bin<kRowThreads, kHistBins>(hist, (uint32_t)k, fs.scan, &s_b1, &s_above1);
+    b1 = s_b1;
+    k1 = (uint32_t)k - s_above1;
+    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;   // becomes h2
+    __syncthreads();
+  }
+  // ordered compaction of candidates (level-1 digit >= b1) into LDS; four
+  // consecutive elements per thread per round
+  uint32_t count = 0;
+  for (int64_t base = 0; base < n; base += 4 * kRowThreads) {
+    const int64_t s0 = base + 4 * (int64_t)threadIdx.x;
+    uint32_t key[4];
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[e] = (s0 + e < n) ? order_key(row[s0 + e]) : 0u;
+      const bool f = (s0 + e < n) && (key[e] >> 20) >= b1;
+      c += f;
+      if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&hist[(key[e] >> 8) & 0xFFF], 1u);
+    }
+    uint32_t tot;
+    uint32_t p = count + block_excl_scan<kRowThreads>(c, fs.scan, &tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool f = (s0 + e < n) && (key[e] >> 20) >= b1;
+      if (f) {
+        if (p < kRowCap) cand[p] = make_uint2(key[e], (uint32_t)(s0 + e));
+        ++p;
+      }
+    }
+    count += tot;
+  }
+  __syncthreads();
+  if (count <= kRowCap) {
+    FlatSource src{cand, (int)count, kRowThreads};
+    final_select<kRowThreads>(src, k, all_mode, b1, k1, hist, fs, out_row);
+  } else {
+    const int64_t seg = (n + kRowThreads - 1) / kRowThreads;
+    RowSource src{row, n, seg, kRowThreads, all_mode ? 0u : b1};
+    final_select<kRowThreads>(src, k, all_mode, b1, k1, hist, fs, out_row);
+  }
+}
+
+bool multi_block(int64_t Lk, int T) {
+  return T <= kTopkMultiRowsMax && cdiv(Lk, kCollectRange) <= kMaxSegs;
+}
+
+}  // namespace
+
+bool topk_multi_block(int64_t Lk, int T) { return multi_block(Lk, T); }
+
+size_t topk_scratch_bytes(int64_t Lk, int T, int k) {
+  (void)k;
+  if (!multi_block(Lk, T)) return 256;
+  const int64_t G = cdiv(Lk, kCollectRange);
+  return (size_t)T * G * kSlotCap * sizeof(uint2) + (size_t)T * G * sizeof(uint32_t) + 256;
+}
+
+hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
+                       void* ws_counters, void* scratch, hipStream_t st, bool hist_ready) {
+  if (!multi_block(Lk, T)) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(T), dim3(kRowThreads), 0, st, scores, ld, Lk, T, k, idx);
+    return hipGetLastError();
+  }
+  TopkCounters ctr = counters_at(ws_counters);
+  const int64_t G = cdiv(Lk, kCollectRange);
+  uint2* slots = reinterpret_cast<uint2*>(scratch);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(slots + (size_t)T * G * kSlotCap);
+  if (!hist_ready) {
+    const int64_t Gh = cdiv(Lk, kHistRange);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)Gh, T), dim3(256), 0, st, scores, ld, Lk, T, ctr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)G, T), dim3(256), 0, st, scores, ld, Lk, T, k, ctr,
+                     slots, cnt, (int)G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_final_kernel, dim3(T), dim3(kFinalThreads), 0, st, scores, ld, Lk, T, k, ctr,
+                     (const uint2*)slots, (const uint32_t*)cnt, (int)G, idx);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dsa.h declares, and rejects bad arguments before launching anything
+(fake pointers below are never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_long_context_index_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+A = 0x10000        # 16-byte aligned fake device address
+MIS = 0x10004      # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libdsa.so not built")
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for name in ("dsa_index_scores", "dsa_topk", "sparse_gqa_attn", "swa_attn", "dsa_decode_step",
+                 "dsa_workspace_bytes", "dsa_workspace_init", "dsa_status_string", "dsa_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        assert hasattr(L, f)
+
+
+def test_status_strings_and_version(L):
+    for code, name in binding.STATUS.items():
+        assert L.dsa_status_string(code).decode().startswith(name)
+    assert b"gfx950" in L.dsa_version()
+
+
+def test_workspace_bytes(L):
+    f = L.dsa_workspace_bytes
+    assert f(binding.OP_INDEX_SCORES, 100, 1, 1, 0) == 0
+    assert f(binding.OP_TOPK, 100, 1, 0, 0) == 0            # k = 0 is invalid
+    assert f(binding.OP_TOPK, 100, 1, 2049, 0) == 0         # k > 2048
+    assert f(binding.OP_DECODE_STEP, 100, 9, 16, 0) == 0    # T > 8
+    a = f(binding.OP_TOPK, 1 << 20, 1, 2048, 0)
+    b = f(binding.OP_TOPK, 1 << 10, 1, 2048, 0)
+    assert a >= b >= (1 << 20)
+    d = f(binding.OP_DECODE_STEP, (1 << 20) + 1, 1, 2048, 0)
+    assert d >= (1 << 20) + 4 * ((1 << 20) + 1)             # counters + scores
+    assert f(binding.OP_SWA_ATTN, 0, 0, 0, 64) > 0
+    assert f(binding.OP_SPARSE_ATTN, 100, 8192, 2048, 0) > 0
+
+
+def test_index_scores_validation(L):
+    s = L.dsa_index_scores
+    assert s(None, A, A, 100, 1, A, 100, None) == 1
+    assert s(A, A, A, 100, 0, A, 100, None) == 2             # T = 0
+    assert s(A, A, A, 5, 6, A, 6, None) == 2                 # T > Lk
+    assert s(A, A, A, 100, 1, A, 99, None) == 2              # ld < Lk
+    assert s(A, A, A, 1 << 31, 1, A, 1 << 31, None) == 2     # Lk too large
+    assert s(MIS, A, A, 100, 1, A, 100, None) == 4
+    assert s(A, A, A, 100, 1, MIS, 100, None) == 4
+
+
+def test_topk_validation(L):
+    t = L.dsa_topk
+    big = 1 << 30
+    assert t(A, 100, 100, 1, 0, A, A, big, None) == 2        # k = 0
+    assert t(A, 100, 100, 1, 2049, A, A, big, None) == 2     # k > 2048
+    assert t(A, 100, 100, 1, 16, A, None, big, None) == 5    # no workspace
+    assert t(A, 100, 100, 1, 16, A, A, 100, None) == 5       # workspace too small
+    assert t(None, 100, 100, 1, 16, A, A, big, None) == 1
+    assert t(A, 100, 100, 1, 16, MIS, A, big, None) == 4
+
+
+def test_attention_validation(L):
+    f = L.sparse_gqa_attn
+    big = 1 << 30
+    assert f(A, A, A, 100, None, 1, 16, None, 0.07, A, None, A, big, None) == 1
+    assert f(A, A, A, 100, A, 1, 0, None, 0.07, A, None, A, big, None) == 2
+    assert f(A, A, A, 100, A, 1, 16, None, float("nan"), A, None, A, big, None) == 2
+    assert f(A, A, A, 100, A, 1, 16, MIS, 0.07, A, None, A, big, None) == 4
+    assert f(A, A, A, 100, A, 1, 16, None, 0.07, A, None, A, 10, None) == 5
+    g = L.swa_attn
+    assert g(A, A, A, 1000, A, A, 4, 0, None, 0.07, A, None, A, big, None) == 2      # window 0
+    assert g(A, A, A, 1000, A, A, 4, 4096, None, 0.07, A, None, A, big, None) == 2   # window > 2048
+    assert g(A, A, A, 1000, None, A, 4, 128, None, 0.07, A, None, A, big, None) == 1
+    assert g(A, A, A, 1000, A, A, 0, 128, None, 0.07, A, None, A, big, None) == 2
+
+
+def test_decode_step_validation(L):
+    f = L.dsa_decode_step
+    big = 1 << 34
+    args = [A, A, A, A, A, A, 100, 1, 16, None, 0.07, A, None, None, None, 0, A, big, None]
+    bad = list(args)
+    bad[7] = 9                                               # T > 8
+    assert f(*bad) == 2
+    bad = list(args)
+    bad[14] = A
+    bad[15] = 50                                             # scores_out with ld < Lk
+    assert f(*bad) == 2
+    bad = list(args)
+    bad[17] = 1000                                           # workspace too small
+    assert f(*bad) == 5
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad) == 1
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(binding.DsaError):
+        binding.dsa_index_scores(x, x, x, 1, 1, scores=torch.zeros(1, 1))

@@ -1,0 +1,354 @@
+"""GPU parity: every entry point of libdsa.so against the fp64 oracle, through
+the C ABI, on seeded inputs that span several tiles plus ragged tails.
+
+Bars (derived in the design notes): index scores within the fp32
+accumulation bound of the 128-term dots and 16-term head sum; top-k on the
+same fp32 scores bit-exact, on independently computed scores equal except in
+the 1e-4 near-tie band; attention within 2e-3 abs + 1e-2 rel element-wise and
+1e-2 relative L2.  Cache rows outside the attended set are NaN-poisoned, so any
+stray read shows up in the output.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_long_context_index_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_NAN = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    return torch.device("cuda", 0)
+
+
+def g(a, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev)
+
+
+def codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3F           # no NaN codes
+    return c
+
+
+def normal_codes(rng, shape, scale=1.0):
+    return synth.encode_e4m3((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def bf16(rng, shape):
+    return synth.encode_bf16(rng.standard_normal(shape).astype(np.float32))
+
+
+# ------------------------------------------------------------ index scores
+
+# Score bounds, relative to sum_h |w_h| sum_d |q_hd k_d|:
+#  * decode path (T <= 8): fp8 widened to bf16 exactly, bf16 MFMA products are
+#    exact and its sums fp32-accurate -> fp32 accumulation bound (128 + 16 terms);
+#  * prefill path (T > 8): the fp8 MFMA adds each group of 8 products after
+#    aligning them to the group's largest exponent and keeps at least 13
+#    fraction bits below it (test_fp8_mfma_accumulation pins this), so each
+#    group loses at most 8 * 2^-13 of its largest product: 2^-10 of the
+#    absolute sum, plus fp32 accumulation across the 16 groups and heads.
+DECODE_REL = 2e-5
+PREFILL_REL = 2.0 ** -10 + 4e-5
+
+
+def score_rel(T):
+    return DECODE_REL if T <= 8 else PREFILL_REL
+
+
+def check_scores(S_gpu, q, w, k, Lk, T):
+    S_ref = oracle.index_scores(q, w, k, Lk, T)
+    bound = oracle.score_error_bound(q, w, k, Lk, T, rel=score_rel(T))
+    S = S_gpu.astype(np.float64)
+    fin = np.isfinite(S_ref)
+    assert np.array_equal(fin, np.isfinite(S)), "causal mask differs"
+    assert np.all(np.isneginf(S[~fin]))
+    err = np.abs(S[fin] - S_ref[fin])
+    assert np.all(err <= bound[fin]), f"max err/bound {np.max(err / bound[fin]):.3f}"
+    return S_ref
+
+
+@pytest.mark.parametrize("T,Lk", [(1, 1), (1, 2), (1, 15), (1, 16), (1, 17), (1, 1000), (2, 129),
+                                  (3, 4097), (4, 5000), (8, 300), (9, 9), (9, 500), (33, 1200),
+                                  (64, 4100), (100, 700)])
+def test_index_scores(dev, T, Lk):
+    rng = np.random.default_rng(1000 + 7 * T + Lk)
+    q = normal_codes(rng, (T, 16, 128))
+    k = normal_codes(rng, (Lk, 128))
+    w = rng.standard_normal((T, 16)).astype(np.float32)
+    ld = Lk + 5
+    S = torch.full((T, ld), 7.0, dtype=torch.float32, device=dev)
+    binding.dsa_index_scores(g(q, dev), g(w, dev), g(k, dev), Lk, T, scores=S, ld=ld)
+    Sh = S.cpu().numpy()
+    assert np.all(Sh[:, Lk:] == 7.0), "columns beyond Lk were written"
+    check_scores(Sh[:, :Lk], q, w, k, Lk, T)
+
+
+def test_index_scores_extreme_codes(dev):
+    rng = np.random.default_rng(5)
+    T, Lk = 4, 777
+    q = codes(rng, (T, 16, 128))                  # the whole code space, incl. +-448 and subnormals
+    k = codes(rng, (Lk, 128))
+    k[:5] = 0x7E                                  # largest magnitude
+    k[5:10] = 0x01                                # smallest subnormal
+    w = (rng.standard_normal((T, 16)) * np.array([1e-3, 1e3] * 8)).astype(np.float32)
+    S = binding.dsa_index_scores(g(q, dev), g(w, dev), g(k, dev), Lk, T)
+    check_scores(S.cpu().numpy(), q, w, k, Lk, T)
+
+
+def test_fp8_codes_decode_exactly_through_both_paths(dev):
+    # every non-NaN e4m3 code as a key against q = 1.0 (head 0) and q = -1.0
+    # (head 1, weight -1): S = relu(c) - relu(-c) = c exactly
+    codes_ = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    for T in (1, 9):
+        q = np.zeros((T, 16, 128), np.uint8)
+        q[:, 0, 0] = 0x38
+        q[:, 1, 0] = 0xB8
+        w = np.zeros((T, 16), np.float32)
+        w[:, 0], w[:, 1] = 1.0, -1.0
+        k = np.zeros((codes_.size + T, 128), np.uint8)
+        k[:codes_.size, 0] = codes_
+        S = binding.dsa_index_scores(g(q, dev), g(w, dev), g(k, dev), k.shape[0], T).cpu().numpy()
+        assert np.array_equal(S[0, :codes_.size].astype(np.float64), oracle.decode_e4m3(codes_))
+
+
+def test_fp8_mfma_accumulation(dev):
+    # q = 1.0 everywhere; key s holds 448 at dim s and 2^-9 elsewhere, so the
+    # exact dot is 448 + 127 * 2^-9.  The decode path (bf16 MFMA on widened
+    # bytes) is exact.  The prefill path (fp8 MFMA) drops the 2^-9 terms that
+    # share an 8-product group with the 448 -- they sit 17 bits below it --
+    # but keeps a 2^-6 next to a 128 (13 bits below).
+    q = np.full((9, 16, 128), 0x38, np.uint8)
+    w = np.zeros((9, 16), np.float32)
+    w[:, 0] = 1.0
+    k = np.full((256 + 9, 128), 0x01, np.uint8)
+    for s_ in range(128):
+        k[s_, s_] = 0x7E
+        k[128 + s_, :] = 0x00
+        k[128 + s_, s_] = 0x08
+        k[128 + s_, (s_ + 1) % 128] = 0x70
+    exact = oracle.decode_e4m3(k[:256]).sum(1)
+    Lk = k.shape[0]
+    S1 = binding.dsa_index_scores(g(q[:1], dev), g(w[:1], dev), g(k, dev), Lk, 1).cpu().numpy()[0, :256]
+    assert np.array_equal(S1.astype(np.float64), exact)
+    S9 = binding.dsa_index_scores(g(q, dev), g(w, dev), g(k, dev), Lk, 9).cpu().numpy()[0, :256]
+    assert np.array_equal(S9[128:].astype(np.float64), exact[128:])
+    lost = exact[:128] - S9[:128].astype(np.float64)
+    assert np.all(lost >= 0) and np.all(lost <= 7 * 2.0 ** -9)
+    assert np.all(lost <= PREFILL_REL * np.abs(oracle.decode_e4m3(k[:128])).sum(1))
+
+
+# ------------------------------------------------------------ top-k
+
+def make_scores(rng, T, Lk, kind):
+    if kind == "normal":
+        S = rng.standard_normal((T, Lk)).astype(np.float32)
+    elif kind == "ties":
+        S = (np.round(rng.standard_normal((T, Lk)) * 3) / 3).astype(np.float32)
+    elif kind == "allequal":
+        S = np.full((T, Lk), 1.25, dtype=np.float32)
+    elif kind == "zeros":
+        S = np.where(rng.random((T, Lk)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        S[:, ::7] = rng.standard_normal((T, len(range(0, Lk, 7)))).astype(np.float32)
+    elif kind == "negative":
+        S = (-np.abs(rng.standard_normal((T, Lk))) * 1e-3).astype(np.float32)
+    elif kind == "wide":
+        S = (rng.standard_normal((T, Lk)) * 10.0 ** rng.integers(-30, 30, (T, Lk))).astype(np.float32)
+    elif kind == "planted":
+        S = rng.standard_normal((T, Lk)).astype(np.float32)
+        hot = rng.choice(Lk, size=min(Lk, 3000), replace=False)
+        S[:, hot] += 50.0
+    else:
+        raise ValueError(kind)
+    for t in range(T):                    # invisible tail is -inf as the indexer writes it
+        S[t, Lk - T + t + 1:] = -np.inf
+    return S
+
+
+def topk_ref_exact(S, Lk, T, k):
+    return oracle.topk(S.astype(np.float64), Lk, T, k)
+
+
+@pytest.mark.parametrize("T,Lk,k,kind", [
+    (1, 1, 1, "normal"), (1, 5, 16, "normal"), (2, 3000, 2048, "normal"), (1, 2048, 2048, "normal"),
+    (1, 2049, 2048, "normal"), (1, 10000, 1, "normal"), (1, 10000, 7, "ties"), (3, 70001, 2048, "ties"),
+    (1, 20000, 2048, "allequal"), (2, 9000, 100, "zeros"), (1, 50000, 2048, "negative"),
+    (4, 131076, 2048, "planted"), (1, 131076, 2048, "wide"), (8, 4096, 512, "normal"),
+    (17, 5000, 2048, "normal"), (40, 33000, 2048, "ties"), (20, 3000, 2048, "allequal"),
+    (24, 20000, 64, "planted"), (32, 100, 2048, "normal"),
+])
+def test_topk_bit_exact(dev, T, Lk, k, kind):
+    rng = np.random.default_rng(zlib.crc32(repr((T, Lk, k, kind)).encode()))
+    S = make_scores(rng, T, Lk, kind)
+    ws = binding.Workspace()
+    idx = binding.dsa_topk(g(S, dev), Lk, T, k, ws=ws).cpu().numpy()
+    ref = topk_ref_exact(S, Lk, T, k)
+    for t in range(T):
+        assert np.array_equal(idx[t], ref[t]), f"row {t}: first diff at {np.flatnonzero(idx[t] != ref[t])[:5]}"
+    # the same workspace again (counters must have been left clean)
+    idx2 = binding.dsa_topk(g(S, dev), Lk, T, k, ws=ws).cpu().numpy()
+    assert np.array_equal(idx, idx2)
+
+
+# ------------------------------------------------------------ sparse attention
+
+def poison_except(K, V, keep):
+    K = K.copy()
+    V = V.copy()
+    mask = np.ones(K.shape[0], dtype=bool)
+    mask[keep] = False
+    K[mask] = BF16_NAN
+    V[mask] = BF16_NAN
+    return K, V
+
+
+@pytest.mark.parametrize("T,Lk,k,use_sink,pad", [
+    (1, 50, 1, True, 0), (1, 50, 7, False, 0), (1, 3000, 64, True, 5), (2, 5000, 2048, True, 0),
+    (3, 8000, 2048, False, 100), (1, 300, 2048, True, 2048 - 300), (4, 20000, 1000, True, 3),
+    (40, 3000, 256, True, 17), (300, 2500, 128, False, 0),
+])
+def test_sparse_attention(dev, T, Lk, k, use_sink, pad):
+    rng = np.random.default_rng(T * 1000 + k)
+    q, K, V = bf16(rng, (T, 64, 192)), bf16(rng, (Lk, 4, 192)), bf16(rng, (Lk, 4, 128))
+    sink = rng.standard_normal(64).astype(np.float32) if use_sink else None
+    nsel = min(k - pad, Lk)
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        sel = np.sort(rng.choice(Lk, size=nsel, replace=False))
+        idx[t, :nsel] = sel
+    keep = np.unique(idx[idx >= 0])
+    Kp, Vp = poison_except(K, V, keep)
+    sc = float(np.float32(1 / math.sqrt(192)))
+    lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    out = binding.sparse_gqa_attn(g(q, dev), g(Kp, dev), g(Vp, dev), Lk, g(idx, dev),
+                                  g(sink, dev) if sink is not None else None, sc, lse=lse)
+    o = out.float().cpu().numpy()
+    o_ref, lse_ref = oracle.sparse_attention(q, K, V, idx, sink, sc)
+    ok, msg = oracle.attn_check(o, o_ref)
+    assert ok, msg
+    l = lse.cpu().numpy()
+    assert np.allclose(l, lse_ref, rtol=1e-4, atol=1e-3), np.max(np.abs(l - lse_ref))
+
+
+def test_sparse_attention_skips_out_of_range_and_empty_rows(dev):
+    rng = np.random.default_rng(9)
+    T, Lk, k = 3, 400, 64
+    q, K, V = bf16(rng, (T, 64, 192)), bf16(rng, (Lk, 4, 192)), bf16(rng, (Lk, 4, 128))
+    sink = rng.standard_normal(64).astype(np.float32)
+    idx = np.full((T, k), -1, dtype=np.int32)
+    idx[0, :10] = np.arange(10) * 30
+    idx[0, 10:14] = [Lk, Lk + 5, -7, 2 ** 31 - 1]        # out of range: skipped
+    idx[1, 5] = 123                                      # one key, not at the start
+    # row 2 stays empty: out = 0, lse = sink
+    sc = 0.07
+    lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    out = binding.sparse_gqa_attn(g(q, dev), g(K, dev), g(V, dev), Lk, g(idx, dev), g(sink, dev), sc, lse=lse)
+    o = out.float().cpu().numpy()
+    clean = np.where((idx >= 0) & (idx < Lk), idx, -1)
+    o_ref, lse_ref = oracle.sparse_attention(q, K, V, clean, sink, sc)
+    assert oracle.attn_check(o[:2], o_ref[:2])[0]
+    assert np.all(o[2] == 0)
+    assert np.allclose(lse.cpu().numpy(), lse_ref, rtol=1e-4, atol=1e-3)
+    # no sink: the empty row has lse = -inf
+    lse2 = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    binding.sparse_gqa_attn(g(q, dev), g(K, dev), g(V, dev), Lk, g(idx, dev), None, sc, lse=lse2)
+    assert np.all(np.isneginf(lse2.cpu().numpy()[2]))
+
+
+# ------------------------------------------------------------ SWA
+
+@pytest.mark.parametrize("window", [128, 1, 37, 200])
+def test_swa_attention(dev, window):
+    rng = np.random.default_rng(window)
+    lens = np.array([1, 5, 127, 128, 129, 1000, 300, 64], dtype=np.int32)
+    B = lens.size
+    starts = np.zeros(B, dtype=np.int64)
+    starts[1:] = np.cumsum(lens.astype(np.int64))[:-1]
+    n_rows = int(lens.sum())
+    K = np.full((n_rows, 8, 192), BF16_NAN, dtype=np.uint16)
+    V = np.full((n_rows, 8, 128), BF16_NAN, dtype=np.uint16)
+    kw, vw = [], []
+    for b in range(B):
+        m = min(int(lens[b]), window)
+        kb, vb = bf16(rng, (m, 8, 192)), bf16(rng, (m, 8, 128))
+        K[starts[b] + lens[b] - m: starts[b] + lens[b]] = kb
+        V[starts[b] + lens[b] - m: starts[b] + lens[b]] = vb
+        kw.append(kb)
+        vw.append(vb)
+    q = bf16(rng, (B, 64, 192))
+    sink = rng.standard_normal(64).astype(np.float32)
+    sc = float(np.float32(1 / math.sqrt(192)))
+    lse = torch.empty((B, 64), dtype=torch.float32, device=dev)
+    out = binding.swa_attn(g(q, dev), g(K, dev), g(V, dev), g(starts, dev), g(lens, dev), window,
+                           g(sink, dev), sc, lse=lse)
+    o_ref, lse_ref = oracle.swa_attention(q, kw, vw, lens, window, sink, sc)
+    ok, msg = oracle.attn_check(out.float().cpu().numpy(), o_ref)
+    assert ok, msg
+    assert np.allclose(lse.cpu().numpy(), lse_ref, rtol=1e-4, atol=1e-3)
+
+
+# ------------------------------------------------------------ fused decode step
+
+def run_decode(dev, d, Lk, T, k, ws=None, sink=True):
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    scores = torch.empty((T, Lk), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    out = binding.dsa_decode_step(g(d["q_idx"], dev), g(d["w"], dev), g(d["k_idx"], dev), g(d["q"], dev),
+                                  g(d["k"], dev), g(d["v"], dev), Lk, T, k,
+                                  g(d["sink"], dev) if sink else None, float(d["sm_scale"]),
+                                  lse=lse, idx_out=idx, scores_out=scores, ws=ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), idx.cpu().numpy(), scores.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_decode(d, Lk, T, k, o, idx, S, sink=True):
+    S_ref = check_scores(S, d["q_idx"], d["w"], d["k_idx"], Lk, T)
+    idx_ref = oracle.topk(S_ref, Lk, T, k)
+    for t in range(T):
+        ok, msg = oracle.topk_check(idx[t], idx_ref[t], S_ref[t, :Lk - T + t + 1], k)
+        assert ok, f"row {t}: {msg}"
+    # the GPU's own selection, bit-exact on the GPU's own fp32 scores
+    assert np.array_equal(idx, topk_ref_exact(S, Lk, T, k))
+    o_ref, _ = oracle.sparse_attention(d["q"], d["k"], d["v"], idx, d["sink"] if sink else None,
+                                       float(d["sm_scale"]))
+    ok, msg = oracle.attn_check(o, o_ref)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("L,T,k,sink", [(3000, 1, 256, True), (5000, 2, 2048, False), (20000, 4, 2048, True),
+                                        (100, 3, 2048, True), (40000, 8, 512, True), (1, 1, 1, True)])
+def test_decode_step(dev, L, T, k, sink):
+    cfg = synth.DecodeConfig("t", L=L, T=T, k=k, plant_frac=0.01, seed=L + T)
+    d = synth.decode_inputs(cfg)
+    o, idx, S, _ = run_decode(dev, d, cfg.Lk, T, k, sink=sink)
+    check_decode(d, cfg.Lk, T, k, o, idx, S, sink=sink)
+
+
+def test_decode_step_deterministic_and_workspace_reuse(dev):
+    cfg = synth.DecodeConfig("t", L=30000, T=2, k=2048, plant_frac=0.01, seed=3)
+    d = synth.decode_inputs(cfg)
+    ws = binding.Workspace()
+    a = run_decode(dev, d, cfg.Lk, 2, 2048, ws=ws)
+    # interleave other calls on the same workspace, then repeat
+    small = synth.DecodeConfig("s", L=500, T=1, k=64, plant_frac=0.0, seed=4)
+    ds = synth.decode_inputs(small)
+    run_decode(dev, ds, small.Lk, 1, 64, ws=ws)
+    S = make_scores(np.random.default_rng(1), 3, 7000, "ties")
+    binding.dsa_topk(g(S, dev), 7000, 3, 300, ws=ws)
+    b = run_decode(dev, d, cfg.Lk, 2, 2048, ws=ws)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
