@@ -93,6 +93,39 @@ __device__ __forceinline__ uint32_t* h1_row(const TopkCounters& c, int rep, int 
 
 // Adds this block's level-1 histogram (in LDS) to replica `rep` of row t and
 // raises the replica's max-bin mark.  All threads call it.
+// Same, for a histogram kept as two 16-bit counters per word (bin b in word
+// b/2, half b&1).
+template <int NT>
+__device__ void flush_level1_packed(const TopkCounters& ctr, int rep, int t, const uint32_t* lh,
+                                    uint32_t* red_sm) {
+  uint32_t* g = h1_row(ctr, rep, t);
+  uint32_t top = 0;
+  for (int i = threadIdx.x; i < kHistBins / 2; i += NT) {
+    const uint32_t c = lh[i];
+    const uint32_t c0 = c & 0xFFFFu, c1 = c >> 16;
+    if (c0) {
+      atomicAdd(&g[2 * i], c0);
+      top = (uint32_t)(2 * i) + 1;
+    }
+    if (c1) {
+      atomicAdd(&g[2 * i + 1], c1);
+      top = (uint32_t)(2 * i) + 2;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t y = __shfl_xor(top, o, 64);
+    top = y > top ? y : top;
+  }
+  if ((threadIdx.x & 63) == 0) red_sm[threadIdx.x >> 6] = top;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < NT / 64; ++i) m = red_sm[i] > m ? red_sm[i] : m;
+    if (m) atomicMax(&ctr.maxbin[rep * kMaxCounterRows + t], m);
+  }
+}
+
 template <int NT>
 __device__ void flush_level1(const TopkCounters& ctr, int rep, int t, const uint32_t* lh, uint32_t* red_sm) {
   uint32_t* g = h1_row(ctr, rep, t);

@@ -32,7 +32,7 @@ namespace dsa {
 namespace {
 
 constexpr int kScanUnroll = 4;   // 16-key tiles per wave in flight
-constexpr int kScanBlocks = 512; // target workgroups of the decode scan
+constexpr int kScanBlocks = 768; // persistent workgroups of the decode scan (3 per CU)
 
 __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   // 32 bytes as two 16-byte loads (only 16-byte alignment is guaranteed)
@@ -80,14 +80,27 @@ __device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
   }
 }
 
+// Decode scan.  Workgroups walk groups of 4*kScanUnroll 16-key tiles in a
+// grid-stride order, so at any moment the chip streams one contiguous stretch
+// of the key cache.  Each wave loads its kScanUnroll tiles with fully
+// coalesced 16-byte loads (1 KiB per instruction), stages them in a
+// wave-private LDS area with a padded row stride, and reads them back in MFMA
+// operand order (key = lane % 16, 32 bytes of k-group lane / 16).  The next
+// group's loads are in flight while the current one is scored.
+//
 // with_hist: also build the level-1 radix histogram of the scores (top-k's
-// first digit); this workgroup adds its counts to replica blockIdx.x % 16.
+// first digit) with two 16-bit counters per LDS word; the workgroup adds its
+// counts to replica blockIdx.x % kHistReplicas.
+constexpr int kStageRow = 144;                     // padded LDS bytes per 128-byte key row
+
 template <int T>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
-    int64_t ld, int64_t tiles_per_wg, TopkCounters ctr, int with_hist) {
-  extern __shared__ uint32_t lhist[];                // [T][4096] when with_hist
+    int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
+  uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
   __shared__ uint32_t red_sm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -95,7 +108,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   const int grp = lane >> 4;
 
   if (with_hist) {
-    for (int i = threadIdx.x; i < T * kHistBins; i += 256) lhist[i] = 0;
+    for (int i = threadIdx.x; i < T * kHistBins / 2; i += 256) lhist[i] = 0;
     __syncthreads();
   }
 
@@ -108,28 +121,38 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     for (int i = 0; i < 4; ++i) wv[t][i] = w[t * 16 + 4 * grp + i];
   }
 
-  const int64_t ntiles = cdiv(Lk, 16);
-  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
-  const int64_t tile_end = tile0 + tiles_per_wg < ntiles ? tile0 + tiles_per_wg : ntiles;
   const int64_t last = Lk - 1;
-  constexpr int64_t kStep = 4 * kScanUnroll;        // tiles per workgroup per batch
-
-  auto load_batch = [&](i32x8* kb, int64_t base) {
+  uint8_t* st = stage + wave * kScanUnroll * 16 * kStageRow;
+  i32x4 buf[2 * kScanUnroll];
+  // wave's keys in group g: [(4g + wave) * 16U, +16U); load i covers 8 keys
+  auto load_group = [&](int64_t g) {
 #pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      int64_t key = (base + u * 4 + wave) * 16 + col;
-      key = key < last ? key : last;                 // ragged tail: stay in bounds
-      kb[u] = load_frag32(k_idx + key * 128 + 32 * grp);
+    for (int i = 0; i < 2 * kScanUnroll; ++i) {
+      int64_t key = (g * 4 + wave) * (kScanUnroll * 16) + 8 * i + (lane >> 3);
+      key = key < last ? key : last;                            // ragged tail: stay in bounds
+      buf[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(k_idx + key * 128 + 16 * (lane & 7)));
     }
   };
-  auto score_batch = [&](const i32x8* kb, int64_t base) {
+
+  int64_t g = blockIdx.x;
+  if (g < ngroups) load_group(g);
+  for (; g < ngroups; g += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < 2 * kScanUnroll; ++i)
+      *reinterpret_cast<i32x4*>(st + (8 * i + (lane >> 3)) * kStageRow + 16 * (lane & 7)) = buf[i];
+    __builtin_amdgcn_wave_barrier();
+    if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
-      const int64_t tile = base + u * 4 + wave;
-      if (tile >= tile_end) continue;                // wave-uniform
-      const int64_t key = tile * 16 + col;
+      const int64_t key = (g * 4 + wave) * (kScanUnroll * 16) + u * 16 + col;
+      const uint8_t* rp = st + (u * 16 + col) * kStageRow + 32 * grp;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(rp);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + 16);
+      i32x8 kr;
+      kr[0] = lo[0]; kr[1] = lo[1]; kr[2] = lo[2]; kr[3] = lo[3];
+      kr[4] = hi[0]; kr[5] = hi[1]; kr[6] = hi[2]; kr[7] = hi[3];
       bf16x8 b[4];
-      widen_fp8(kb[u], b);
+      widen_fp8(kr, b);
       float s[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -144,27 +167,19 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         for (int t = 0; t < T; ++t)
           if ((t & 3) == grp) {
             scores[(int64_t)t * ld + key] = s[t];
-            if (with_hist && key <= Lk - T + t)
-              atomicAdd(&lhist[t * kHistBins + (order_key(s[t]) >> 20)], 1u);
+            if (with_hist && key <= Lk - T + t) {
+              const uint32_t bin = order_key(s[t]) >> 20;
+              atomicAdd(&lhist[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
+            }
           }
       }
     }
-  };
-
-  // two batches in flight: the next batch's loads are issued before the
-  // current batch is scored
-  i32x8 ka[kScanUnroll], kb2[kScanUnroll];
-  if (tile0 < tile_end) load_batch(ka, tile0);
-  for (int64_t base = tile0; base < tile_end; base += 2 * kStep) {
-    if (base + kStep < tile_end) load_batch(kb2, base + kStep);
-    score_batch(ka, base);
-    if (base + 2 * kStep < tile_end) load_batch(ka, base + 2 * kStep);
-    if (base + kStep < tile_end) score_batch(kb2, base + kStep);
+    __builtin_amdgcn_wave_barrier();
   }
   if (with_hist) {
     __syncthreads();
     for (int t = 0; t < T; ++t) {
-      flush_level1<256>(ctr, blockIdx.x % kHistReplicas, t, lhist + t * kHistBins, red_sm);
+      flush_level1_packed<256>(ctr, blockIdx.x % kHistReplicas, t, lhist + t * (kHistBins / 2), red_sm);
       __syncthreads();
     }
   }
@@ -249,14 +264,15 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
   if (T <= kDecodeTMax) {
     if (with_hist && T > kScanHistTMax) return hipErrorInvalidValue;
     const int64_t ntiles = cdiv(Lk, 16);
-    const int64_t step = 4 * kScanUnroll;
-    // about kScanBlocks workgroups, each a contiguous range of whole steps
-    const int64_t tpw = cdiv(cdiv(ntiles, kScanBlocks), step) * step;
-    const dim3 grid((unsigned)cdiv(ntiles, tpw));
-    const size_t lds = with_hist ? (size_t)T * kHistBins * sizeof(uint32_t) : 0;
+    const int64_t ngroups = cdiv(ntiles, 4 * kScanUnroll);
+    // 16-bit histogram counters: a workgroup must see fewer than 65536 keys
+    const int64_t grid = ngroups < kScanBlocks ? ngroups : kScanBlocks;
+    if (with_hist && cdiv(ngroups, grid) * 4 * kScanUnroll * 16 >= 65536) return hipErrorInvalidValue;
+    const size_t lds = (size_t)4 * kScanUnroll * 16 * kStageRow +
+                       (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
     switch (T) {
 #define DSA_SCAN_CASE(n) \
-  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, grid, dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, tpw, ctr, with_hist); break;
+  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, dim3((unsigned)grid), dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, ngroups, ctr, with_hist); break;
       DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
       DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
 #undef DSA_SCAN_CASE

@@ -37,7 +37,7 @@ constexpr int kCollectPer = 16;                                 // per thread
 constexpr int kCollectRange = kCollectThreads * kCollectPer;    // per block
 constexpr int kSlotCap = 512;                                   // candidates per block
 constexpr int kMaxSegs = 1024;                                  // blocks per row (multi-block path)
-constexpr int kCandCap = 6144;                                  // LDS candidates of the final block
+constexpr int kCandCap = 16384;                                 // LDS candidates of the final block
 constexpr int kHistRange = 2048;                                // per hist block
 constexpr int kRowThreads = 1024;
 constexpr int kRowCap = 6144;                                   // LDS candidates per row
@@ -273,51 +273,76 @@ __device__ void find_b1(const TopkCounters& ctr, int t, uint32_t need, uint32_t*
 
 // Each block compacts, in index order, the keys of its range whose level-1
 // digit reaches the threshold digit into its own slot, and adds the level-2
-// digits of the boundary bin to the row's level-2 histogram.
+// digits of the boundary bin to the row's level-2 histogram.  Element e of
+// thread j is key lo + 256 e + j (coalesced loads); the index order is (e, j),
+// so the compaction offsets come from per-wave ballots and one 64-entry scan.
 __global__ __launch_bounds__(256) void topk_collect_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
-    uint2* __restrict__ slots, uint32_t* __restrict__ slot_cnt, int G) {
+    uint2* __restrict__ slots, uint32_t* __restrict__ slot_cnt, uint32_t* __restrict__ rowinfo, int G) {
   __shared__ uint32_t h2[kHistBins];
   __shared__ uint32_t scan_sm[4];
+  __shared__ uint32_t wcnt[kCollectPer * 4];
   __shared__ uint32_t s_b1, s_above1;
   const int t = blockIdx.y;
   const int wg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int64_t n = Lk - T + t + 1;
   const bool all_mode = n <= (int64_t)k;
   const float* row = scores + (int64_t)t * ld;
-  const int64_t lo = (int64_t)wg * kCollectRange + (int64_t)threadIdx.x * kCollectPer;
+  const int64_t lo = (int64_t)wg * kCollectRange + threadIdx.x;
 
   float v[kCollectPer];
 #pragma unroll
-  for (int e = 0; e < kCollectPer; ++e) v[e] = (lo + e < n) ? row[lo + e] : 0.0f;
+  for (int e = 0; e < kCollectPer; ++e) v[e] = (lo + 256 * e < n) ? row[lo + 256 * e] : 0.0f;
   for (int i = threadIdx.x; i < kHistBins; i += 256) h2[i] = 0;
 
   uint32_t b1 = 0;
   if (!all_mode) {
     find_b1<256>(ctr, t, (uint32_t)k, scan_sm, &s_b1, &s_above1);
     b1 = s_b1;
+    if (wg == 0 && threadIdx.x == 0) {
+      rowinfo[2 * t] = s_b1;
+      rowinfo[2 * t + 1] = s_above1;
+    }
   } else {
     __syncthreads();
   }
 
   uint32_t key[kCollectPer];
-  uint32_t cnt = 0;
+  uint64_t mask[kCollectPer];
 #pragma unroll
   for (int e = 0; e < kCollectPer; ++e) {
     key[e] = order_key(v[e]);
-    const bool f = (lo + e < n) && (key[e] >> 20) >= b1;
-    cnt += f;
+    const bool f = (lo + 256 * e < n) && (key[e] >> 20) >= b1;
+    mask[e] = __ballot(f);
     if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&h2[(key[e] >> 8) & 0xFFF], 1u);
+    if (lane == 0) wcnt[e * 4 + wave] = (uint32_t)__popcll(mask[e]);
   }
-  uint32_t total;
-  uint32_t pos = block_excl_scan<256>(cnt, scan_sm, &total);
+  __syncthreads();
+  // exclusive prefix of the 64 (e, wave) counts, in index order
+  __shared__ uint32_t wpre[kCollectPer * 4 + 1];
+  if (wave == 0) {
+    const uint32_t c = wcnt[lane];
+    uint32_t x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    wpre[lane] = x - c;
+    if (lane == 63) wpre[64] = x;
+  }
+  __syncthreads();
+  const uint32_t total = wpre[64];
   uint2* my_slots = slots + ((size_t)t * G + wg) * kSlotCap;
 #pragma unroll
   for (int e = 0; e < kCollectPer; ++e) {
-    const bool f = (lo + e < n) && (key[e] >> 20) >= b1;
-    if (f) {
-      if (pos < kSlotCap) my_slots[pos] = make_uint2(key[e], (uint32_t)(lo + e));
-      ++pos;
+    if ((mask[e] >> lane) & 1ull) {
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask[e] >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask[e], 0u));
+      const uint32_t pos = wpre[e * 4 + wave] + below;
+      if (pos < kSlotCap) my_slots[pos] = make_uint2(key[e], (uint32_t)(lo + 256 * e));
     }
   }
   if (threadIdx.x == 0) {
@@ -334,81 +359,64 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
 }
 
 constexpr int kFinalThreads = 1024;
-static_assert(kMaxSegs <= kFinalThreads, "one slot count per thread");
+static_assert(kMaxSegs <= kFinalThreads, "one slot per thread");
 
 struct FinalKernelShared {
   uint2 cand[kCandCap];
-  uint32_t offs[kMaxSegs + 1];
   FinalShared fs;
-  uint32_t b1, above1;
 };
 
-// One block per row: gathers the ordered candidates of all slots into LDS
-// (independent loads), resolves the exact threshold and emits the row, then
-// leaves the row's counters zeroed.
+// Grid (T, 1 + kHistReplicas).  Block (t, 0) gathers the ordered candidates of
+// all slots of row t into LDS, resolves the exact threshold and emits the row;
+// blocks (t, 1 + r) clear level-1 replica r of the row for the next call.
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
-    const uint2* __restrict__ slots, const uint32_t* __restrict__ slot_cnt, int G, int32_t* __restrict__ idx) {
+    const uint2* __restrict__ slots, const uint32_t* __restrict__ slot_cnt, const uint32_t* __restrict__ rowinfo,
+    int G, int32_t* __restrict__ idx) {
   __shared__ FinalKernelShared sh;
   const int t = blockIdx.x;
+  if (blockIdx.y > 0) {
+    const int r = blockIdx.y - 1;
+    uint4* z = reinterpret_cast<uint4*>(h1_row(ctr, r, t));
+    for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z[i] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0) ctr.maxbin[r * kMaxCounterRows + t] = 0;
+    return;
+  }
   const int64_t n = Lk - T + t + 1;
   const bool all_mode = n <= (int64_t)k;
   const float* row = scores + (int64_t)t * ld;
   int32_t* out_row = idx + (size_t)t * k;
+  // every independent load first
   const uint32_t ovf = ctr.overflow[t];
-  const uint32_t c_own = (int)threadIdx.x < G ? slot_cnt[(size_t)t * G + threadIdx.x] : 0u;
+  const uint32_t b1 = all_mode ? 0u : rowinfo[2 * t];
+  const uint32_t above1 = all_mode ? 0u : rowinfo[2 * t + 1];
+  const int j = threadIdx.x;
+  const uint32_t c_own = j < G ? slot_cnt[(size_t)t * G + j] : 0u;
+  const uint32_t* g2 = ctr.h2 + (size_t)t * kHistBins;
 
-  uint32_t b1 = 0, k1 = 0;
-  if (!all_mode) {
-    find_b1<kFinalThreads>(ctr, t, (uint32_t)k, sh.fs.scan, &sh.b1, &sh.above1);
-    b1 = sh.b1;
-    k1 = (uint32_t)k - sh.above1;
-  }
   uint32_t M;
   const uint32_t base = block_excl_scan<kFinalThreads>(c_own, sh.fs.scan, &M);
-  if ((int)threadIdx.x < G) sh.offs[threadIdx.x] = base;
-  if (threadIdx.x == 0) sh.offs[G] = M;
-  __syncthreads();
-  const uint32_t* g2 = ctr.h2 + (size_t)t * kHistBins;
   if (!ovf && M <= (uint32_t)kCandCap) {
-    const uint2* rs = slots + (size_t)t * G * kSlotCap;
-    for (uint32_t e0 = threadIdx.x; e0 < M; e0 += 8 * kFinalThreads) {
+    // thread j copies slot j, eight independent loads at a time
+    const uint2* sp = slots + ((size_t)t * G + (j < G ? j : 0)) * kSlotCap;
+    for (uint32_t i0 = 0; i0 < c_own; i0 += 8) {
       uint2 buf[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t e = e0 + j * kFinalThreads;
-        buf[j] = make_uint2(0u, 0u);
-        if (e < M) {
-          int lo_s = 0, hi_s = G - 1;                    // last segment with offs <= e
-          while (lo_s < hi_s) {
-            const int mid = (lo_s + hi_s + 1) >> 1;
-            if (sh.offs[mid] <= e) lo_s = mid; else hi_s = mid - 1;
-          }
-          buf[j] = rs[(size_t)lo_s * kSlotCap + (e - sh.offs[lo_s])];
-        }
-      }
+      for (int i = 0; i < 8; ++i) buf[i] = i0 + i < c_own ? sp[i0 + i] : make_uint2(0u, 0u);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t e = e0 + j * kFinalThreads;
-        if (e < M) sh.cand[e] = buf[j];
-      }
+      for (int i = 0; i < 8; ++i)
+        if (i0 + i < c_own) sh.cand[base + i0 + i] = buf[i];
     }
     __syncthreads();
     FlatSource src{sh.cand, (int)M, kFinalThreads};
-    final_select<kFinalThreads>(src, k, all_mode, b1, k1, g2, sh.fs, out_row);
+    final_select<kFinalThreads>(src, k, all_mode, b1, (uint32_t)k - above1, g2, sh.fs, out_row);
   } else {
-    RowSource src{row, n, kCollectRange, G, all_mode ? 0u : b1};
-    final_select<kFinalThreads>(src, k, all_mode, b1, k1, g2, sh.fs, out_row);
+    RowSource src{row, n, kCollectRange, G, b1};
+    final_select<kFinalThreads>(src, k, all_mode, b1, (uint32_t)k - above1, g2, sh.fs, out_row);
   }
-  // leave the row's counters zeroed for the next call
   __syncthreads();
-  for (int r = 0; r < kHistReplicas; ++r) {
-    uint4* z = reinterpret_cast<uint4*>(h1_row(ctr, r, t));
-    for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z[i] = make_uint4(0, 0, 0, 0);
-  }
   uint4* z2 = reinterpret_cast<uint4*>(ctr.h2 + (size_t)t * kHistBins);
   for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z2[i] = make_uint4(0, 0, 0, 0);
-  if (threadIdx.x < kHistReplicas) ctr.maxbin[threadIdx.x * kMaxCounterRows + t] = 0;
   if (threadIdx.x == 0) ctr.overflow[t] = 0;
 }
 
@@ -482,13 +490,12 @@ bool multi_block(int64_t Lk, int T) {
 
 }  // namespace
 
-bool topk_multi_block(int64_t Lk, int T) { return multi_block(Lk, T); }
 
 size_t topk_scratch_bytes(int64_t Lk, int T, int k) {
   (void)k;
   if (!multi_block(Lk, T)) return 256;
   const int64_t G = cdiv(Lk, kCollectRange);
-  return (size_t)T * G * kSlotCap * sizeof(uint2) + (size_t)T * G * sizeof(uint32_t) + 256;
+  return (size_t)T * G * kSlotCap * sizeof(uint2) + (size_t)T * G * sizeof(uint32_t) + (size_t)T * 8 + 256;
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
@@ -501,19 +508,23 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k
   const int64_t G = cdiv(Lk, kCollectRange);
   uint2* slots = reinterpret_cast<uint2*>(scratch);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(slots + (size_t)T * G * kSlotCap);
+  uint32_t* rowinfo = cnt + (size_t)T * G;
+  hipError_t e;
   if (!hist_ready) {
     const int64_t Gh = cdiv(Lk, kHistRange);
     hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)Gh, T), dim3(256), 0, st, scores, ld, Lk, T, ctr);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)G, T), dim3(256), 0, st, scores, ld, Lk, T, k, ctr,
-                     slots, cnt, (int)G);
-  hipError_t e = hipGetLastError();
+                     slots, cnt, rowinfo, (int)G);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(T), dim3(kFinalThreads), 0, st, scores, ld, Lk, T, k, ctr,
-                     (const uint2*)slots, (const uint32_t*)cnt, (int)G, idx);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(T, 1 + kHistReplicas), dim3(kFinalThreads), 0, st, scores, ld, Lk, T,
+                     k, ctr, (const uint2*)slots, (const uint32_t*)cnt, (const uint32_t*)rowinfo, (int)G, idx);
   return hipGetLastError();
 }
+
+bool topk_multi_block(int64_t Lk, int T) { return multi_block(Lk, T); }
 
 }  // namespace dsa
