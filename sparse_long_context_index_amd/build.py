@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "index_scores.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "index_scores.hip", "topk.hip", "attn.hip", "decode.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

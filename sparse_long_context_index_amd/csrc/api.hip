@@ -5,6 +5,7 @@
 
 #include "dsa_common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
@@ -41,8 +42,24 @@ dsa_status check_attn_args(const void* q, const void* k, const void* v, const vo
 }
 
 struct DecodeLayout {
-  size_t scores, idx, topk, attn, total;
+  size_t scores, idx, topk, attn, lkeys, lidx, lcount, part, total;
 };
+
+constexpr int kScanListTMax = 4;                // rows the fused list path serves
+constexpr size_t kScanListLdsMax = 80 * 1024;   // keeps two scan workgroups per CU
+constexpr int kScanListsMax = 512;
+
+// The fused path: the scan writes per-workgroup top lists and one kernel
+// selects, attends and merges.  It needs the scan's LDS to stay small and
+// about k / 8 or more scan workgroups, so that a list of 32 rarely fills up
+// (a full list that keeps its last entry sends the selection to the slow
+// full-row re-selection).  Otherwise: histogram top-k, then attention.
+bool use_list_path(int64_t Lk, int T, int k) {
+  if (T > kScanListTMax) return false;
+  const int grid = scan_grid(Lk);
+  const size_t lds = scan_lds_bytes(Lk, T, true);
+  return lds <= kScanListLdsMax && grid <= kScanListsMax && (int64_t)k <= (int64_t)8 * grid;
+}
 
 DecodeLayout decode_layout(int64_t Lk, int T, int k) {
   DecodeLayout d;
@@ -55,6 +72,14 @@ DecodeLayout decode_layout(int64_t Lk, int T, int k) {
   off += align_up(topk_scratch_bytes(Lk, T, k));
   d.attn = off;
   off += align_up(attn_scratch_bytes(T, k, DSA_KV_HEADS));
+  d.lkeys = off;
+  off += align_up((size_t)T * kScanListsMax * kListM * sizeof(uint32_t));
+  d.lidx = off;
+  off += align_up((size_t)T * kScanListsMax * kListM * sizeof(uint32_t));
+  d.lcount = off;
+  off += align_up((size_t)T * kScanListsMax * sizeof(uint32_t));
+  d.part = off;
+  off += align_up((size_t)T * DSA_KV_HEADS * decode_chunks(k) * (16 + 16 + 16 * 128) * sizeof(float));
   d.total = off;
   return d;
 }
@@ -197,6 +222,24 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
   hipStream_t st = as_stream(stream);
 
+  if (use_list_path(Lk, T, k)) {
+    ScanLists sl;
+    sl.keys = reinterpret_cast<uint32_t*>(base + L.lkeys);
+    sl.idx = reinterpret_cast<uint32_t*>(base + L.lidx);
+    sl.count = reinterpret_cast<uint32_t*>(base + L.lcount);
+    hipError_t e = launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld, st, nullptr, sl);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    DecodeArgs d{};
+    d.a.q = q; d.a.k = k_cache; d.a.v = v_cache; d.a.n_rows = Lk; d.a.T = T; d.a.k_len = k;
+    d.a.sink = sink; d.a.sm_scale = sm_scale; d.a.out = out; d.a.lse = lse;
+    d.scores = scores; d.ld = ld; d.Lk = Lk; d.k = k;
+    d.lkeys = sl.keys; d.lidx = sl.idx; d.lcount = sl.count; d.nlists = scan_grid(Lk);
+    d.idx_out = idx_out;
+    d.part = reinterpret_cast<float*>(base + L.part);
+    d.unit_ctr = reinterpret_cast<uint32_t*>(base + kUnitCtrOffset);
+    d.n_chunks = decode_chunks(k);
+    return hip_status(launch_decode_attend(d, st));
+  }
   // up to kScanHistTMax tokens the scan also builds the top-k's level-1 histogram
   const bool fused = T <= kScanHistTMax && topk_multi_block(Lk, T);
   hipError_t e = launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld, st, fused ? base : nullptr);

@@ -26,13 +26,14 @@
 //    and bounded in the tests).
 #include "dsa_common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
 namespace {
 
 constexpr int kScanUnroll = 4;   // 16-key tiles per wave in flight
-constexpr int kScanBlocks = 768; // persistent workgroups of the decode scan (3 per CU)
+constexpr int kScanBlocks = 512; // persistent workgroups of the decode scan (2 per CU)
 
 __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   // 32 bytes as two 16-byte loads (only 16-byte alignment is guaranteed)
@@ -80,27 +81,47 @@ __device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
   }
 }
 
-// Decode scan.  Workgroups walk groups of 4*kScanUnroll 16-key tiles in a
-// grid-stride order, so at any moment the chip streams one contiguous stretch
-// of the key cache.  Each wave loads its kScanUnroll tiles with fully
-// coalesced 16-byte loads (1 KiB per instruction), stages them in a
-// wave-private LDS area with a padded row stride, and reads them back in MFMA
-// operand order (key = lane % 16, 32 bytes of k-group lane / 16).  The next
-// group's loads are in flight while the current one is scored.
+// Decode scan.  16-key tiles are dealt round-robin to the workgroups (tile j
+// belongs to workgroup j % G), so at any moment the chip streams one
+// contiguous stretch of the key cache and any run of consecutive keys is
+// spread over many workgroups.  Each wave takes kScanUnroll of its
+// workgroup's tiles per step, loads each with fully coalesced 16-byte loads
+// (1 KiB per instruction), stages it in a wave-private LDS area with a padded
+// row stride, and reads it back in MFMA operand order (key = lane % 16, 32
+// bytes of k-group lane / 16).  The next step's loads are in flight while the
+// current one is scored.
 //
 // with_hist: also build the level-1 radix histogram of the scores (top-k's
 // first digit) with two 16-bit counters per LDS word; the workgroup adds its
 // counts to replica blockIdx.x % kHistReplicas.
+//
+// lists (optional, exclusive with with_hist): the workgroup also keeps its
+// scores in LDS and, at the end, writes for every query row its exact local
+// top-kListM keys as a list sorted by (score desc, index asc) of order keys
+// and key indices, with a count word (bit 31: more than kListM of its keys
+// were visible).  The fused decode step selects the global top-k from
+// these lists.
 constexpr int kStageRow = 144;                     // padded LDS bytes per 128-byte key row
+
+constexpr int kCandCap = 256;                      // candidates ranked directly in the list epilogue
+
+struct ListShared {
+  RadixShared rs;
+  alignas(16) uint32_t key[kCandCap];
+  alignas(16) uint32_t idx[kCandCap];
+  uint32_t n;
+  uint32_t red[4];
+};
 
 template <int T>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
-    int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist) {
+    int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist, ScanLists lists) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
+  float* lsc = reinterpret_cast<float*>(smem + 4 * kScanUnroll * 16 * kStageRow);           // [T][cap]
   __shared__ uint32_t red_sm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -122,29 +143,41 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   }
 
   const int64_t last = Lk - 1;
+  const int64_t ntiles = cdiv(Lk, 16);
+  const int64_t G = gridDim.x;
   uint8_t* st = stage + wave * kScanUnroll * 16 * kStageRow;
   i32x4 buf[2 * kScanUnroll];
-  // wave's keys in group g: [(4g + wave) * 16U, +16U); load i covers 8 keys
-  auto load_group = [&](int64_t g) {
+  // local tile lt of this workgroup is global tile blockIdx.x + G * lt; step
+  // `it` gives wave w the local tiles 16 it + kScanUnroll w + u; load i covers
+  // 8 keys of tile i / 2
+  auto tile_of = [&](int it, int u) -> int64_t {
+    return (int64_t)blockIdx.x + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
+  };
+  auto load_step = [&](int it) {
 #pragma unroll
     for (int i = 0; i < 2 * kScanUnroll; ++i) {
-      int64_t key = (g * 4 + wave) * (kScanUnroll * 16) + 8 * i + (lane >> 3);
+      int64_t key = tile_of(it, i >> 1) * 16 + 8 * (i & 1) + (lane >> 3);
       key = key < last ? key : last;                            // ragged tail: stay in bounds
       buf[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(k_idx + key * 128 + 16 * (lane & 7)));
     }
   };
 
-  int64_t g = blockIdx.x;
-  if (g < ngroups) load_group(g);
-  for (; g < ngroups; g += gridDim.x) {
+  (void)ngroups;
+  const int64_t n_local = cdiv(ntiles - blockIdx.x, G);         // tiles of this workgroup
+  const int n_steps = (int)cdiv(n_local, 4 * kScanUnroll);
+  int iter = 0;
+  if (n_steps > 0) load_step(0);
+  for (; iter < n_steps; ++iter) {
 #pragma unroll
     for (int i = 0; i < 2 * kScanUnroll; ++i)
       *reinterpret_cast<i32x4*>(st + (8 * i + (lane >> 3)) * kStageRow + 16 * (lane & 7)) = buf[i];
     __builtin_amdgcn_wave_barrier();
-    if (g + gridDim.x < ngroups) load_group(g + gridDim.x);
+    if (iter + 1 < n_steps) load_step(iter + 1);
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
-      const int64_t key = (g * 4 + wave) * (kScanUnroll * 16) + u * 16 + col;
+      const int64_t tile = tile_of(iter, u);
+      if (tile >= ntiles) continue;                             // wave-uniform
+      const int64_t key = tile * 16 + col;
       const uint8_t* rp = st + (u * 16 + col) * kStageRow + 32 * grp;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(rp);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + 16);
@@ -167,6 +200,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         for (int t = 0; t < T; ++t)
           if ((t & 3) == grp) {
             scores[(int64_t)t * ld + key] = s[t];
+            if (lists.keys) lsc[t * lists.cap + (iter * 4 * kScanUnroll + wave * kScanUnroll + u) * 16 + col] = s[t];
             if (with_hist && key <= Lk - T + t) {
               const uint32_t bin = order_key(s[t]) >> 20;
               atomicAdd(&lhist[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -180,6 +214,136 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     __syncthreads();
     for (int t = 0; t < T; ++t) {
       flush_level1_packed<256>(ctr, blockIdx.x % kHistReplicas, t, lhist + t * (kHistBins / 2), red_sm);
+      __syncthreads();
+    }
+  }
+  if (lists.keys) {
+    __syncthreads();
+    ListShared& ls = *reinterpret_cast<ListShared*>(smem + 4 * kScanUnroll * 16 * kStageRow +
+                                                     (size_t)T * lists.cap * sizeof(float));
+    // local position i is key (i % 16) of local tile i / 16, i.e. of global
+    // tile bx + G (i / 16); key indices fit 32 bits (Lk < 2^31)
+    const uint32_t bx = blockIdx.x, G32 = gridDim.x;
+    const int n_loc = iter * 4 * kScanUnroll * 16;
+    auto gidx = [&](int i) -> uint32_t { return (bx + G32 * ((uint32_t)i >> 4)) * 16u + ((uint32_t)i & 15u); };
+    for (int t = 0; t < T; ++t) {
+      const uint32_t P = (uint32_t)(Lk - T + t + 1);            // keys visible to row t
+      const float* lt = lsc + t * lists.cap;
+      auto key_at = [&](int i) -> uint32_t { return gidx(i) < P ? order_key(lt[i]) : 0u; };
+      // visible keys of this workgroup: whole tiles below P / 16, plus the partial one
+      const uint32_t F = P >> 4, rem = P & 15u;
+      uint32_t n_vis = F > bx ? (F - bx + G32 - 1) / G32 * 16u : 0u;
+      if (rem && F >= bx && (F - bx) % G32 == 0) n_vis += rem;
+      const bool full = n_vis > (uint32_t)kListM;
+      // Candidates are the visible keys >= L0, a lower bound of the kListM-th
+      // largest: the smallest of the maxima of 32 groups of 8 threads (each
+      // group holds a key at least that large).  They are ranked directly
+      // when few; otherwise a radix descent finds the threshold first.
+      uint32_t L0 = 1u;                                         // key 0: not visible
+      if (full) {
+        uint32_t mx = 0;
+        for (int i = threadIdx.x; i < n_loc; i += 256) {
+          const uint32_t kk = key_at(i);
+          mx = mx > kk ? mx : kk;
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, 64);
+          mx = mx > y ? mx : y;
+        }
+        const uint32_t wmin = wave_incl_minmax<false>(mx);
+        if ((threadIdx.x & 63) == 63) ls.red[threadIdx.x >> 6] = wmin;
+        __syncthreads();
+        uint32_t g = ls.red[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) g = g < ls.red[w] ? g : ls.red[w];
+        L0 = g > 1u ? g : 1u;
+      }
+      if (threadIdx.x == 0) ls.n = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < n_loc; i += 256) {          // n_loc is a multiple of 256
+        const uint32_t key = key_at(i);
+        const bool pass = key >= L0;
+        const uint64_t m = __ballot(pass);
+        uint32_t base = 0;
+        if ((threadIdx.x & 63) == 0 && m) base = atomicAdd(&ls.n, (uint32_t)__popcll(m));
+        base = (uint32_t)__shfl((int)base, 0, 64);
+        const uint32_t p = base + (uint32_t)__popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
+        if (pass && p < (uint32_t)kCandCap) {
+          ls.key[p] = key;
+          ls.idx[p] = gidx(i);
+        }
+      }
+      __syncthreads();
+      const uint32_t C = ls.n;
+      __syncthreads();
+      if (C > (uint32_t)kCandCap) {
+        // many candidates: exact threshold by radix descent, then collect the kListM kept
+        uint32_t tau = 0, tau2 = 0, r, eq;
+        bool split = false;
+        radix_threshold<256>(key_at, n_loc, (uint32_t)kListM, ls.rs, &tau, &r, &eq);
+        if (eq > r) {                 // keep the r lowest key indices among the ties
+          uint32_t r2, eq2;
+          radix_threshold<256>([&](int i) { return key_at(i) == tau ? ~gidx(i) : 0u; }, n_loc, r, ls.rs, &tau2,
+                               &r2, &eq2);
+          split = true;
+        }
+        if (threadIdx.x == 0) ls.n = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n_loc; i += 256) {
+          const uint32_t key = key_at(i);
+          if (key > tau || (key == tau && (!split || ~gidx(i) >= tau2))) {
+            const uint32_t p = atomicAdd(&ls.n, 1u);
+            if (p < (uint32_t)kListM) {
+              ls.key[p] = key;
+              ls.idx[p] = gidx(i);
+            }
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t nc = C > (uint32_t)kCandCap ? (ls.n < (uint32_t)kListM ? ls.n : (uint32_t)kListM) : C;
+      const uint32_t kept = nc < (uint32_t)kListM ? nc : (uint32_t)kListM;
+      // rank in (key desc, index asc) order; the first kListM ranks form the
+      // list.  The candidate arrays are padded to a multiple of 16 with key 0,
+      // which ranks below every candidate, so the reads go 16 at a time.
+      const uint32_t ncp = (nc + 15u) & ~15u;
+      if (threadIdx.x >= nc && threadIdx.x < ncp) {
+        ls.key[threadIdx.x] = 0u;
+        ls.idx[threadIdx.x] = 0xFFFFFFFFu;
+      }
+      __syncthreads();
+      if (threadIdx.x < nc) {
+        const uint32_t key = ls.key[threadIdx.x], id = ls.idx[threadIdx.x];
+        uint32_t rank = 0;
+        for (uint32_t j0 = 0; j0 < ncp; j0 += 16) {
+          uint4 k4[4], i4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            k4[q] = *reinterpret_cast<const uint4*>(&ls.key[j0 + 4 * q]);
+            i4[q] = *reinterpret_cast<const uint4*>(&ls.idx[j0 + 4 * q]);
+          }
+          // branch-free: (kj > key) | ((kj == key) & (ij < id))
+          auto before = [&](uint32_t kj, uint32_t ij) {
+            return (uint32_t)(kj > key) | ((uint32_t)(kj == key) & (uint32_t)(ij < id));
+          };
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
+                    before(k4[q].w, i4[q].w);
+        }
+        if (rank < (uint32_t)kListM) {
+          const size_t o = ((size_t)t * kListM + rank) * G32 + bx;
+          lists.keys[o] = key;
+          lists.idx[o] = id;
+        }
+      }
+      if (threadIdx.x >= kept && threadIdx.x < kListM) {       // unused entries
+        const size_t o = ((size_t)t * kListM + threadIdx.x) * G32 + bx;
+        lists.keys[o] = 0u;
+        lists.idx[o] = 0xFFFFFFFFu;
+      }
+      if (threadIdx.x == 0) lists.count[(size_t)t * G32 + bx] = kept | (full ? 0x80000000u : 0u);
       __syncthreads();
     }
   }
@@ -256,23 +420,41 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(
 
 }  // namespace
 
+int scan_grid(int64_t Lk) {
+  const int64_t ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
+  return (int)(ngroups < kScanBlocks ? ngroups : kScanBlocks);
+}
+
+int scan_list_cap(int64_t Lk) {
+  const int64_t local_tiles = cdiv(cdiv(Lk, 16), scan_grid(Lk));   // workgroup 0 has the most
+  return (int)(cdiv(local_tiles, 4 * kScanUnroll) * 4 * kScanUnroll * 16);
+}
+
+size_t scan_lds_bytes(int64_t Lk, int T, bool lists) {
+  return (size_t)4 * kScanUnroll * 16 * kStageRow +
+         (lists ? (size_t)T * scan_list_cap(Lk) * sizeof(float) + sizeof(ListShared) : 0);
+}
+
 hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                                int64_t Lk, int T, float* scores, int64_t ld, hipStream_t st,
-                               void* topk_counters) {
+                               void* topk_counters, ScanLists lists) {
   const int with_hist = topk_counters != nullptr;
+  if (with_hist && lists.keys) return hipErrorInvalidValue;
   const TopkCounters ctr = topk_counters ? counters_at(topk_counters) : TopkCounters{};
   if (T <= kDecodeTMax) {
     if (with_hist && T > kScanHistTMax) return hipErrorInvalidValue;
     const int64_t ntiles = cdiv(Lk, 16);
     const int64_t ngroups = cdiv(ntiles, 4 * kScanUnroll);
     // 16-bit histogram counters: a workgroup must see fewer than 65536 keys
-    const int64_t grid = ngroups < kScanBlocks ? ngroups : kScanBlocks;
-    if (with_hist && cdiv(ngroups, grid) * 4 * kScanUnroll * 16 >= 65536) return hipErrorInvalidValue;
-    const size_t lds = (size_t)4 * kScanUnroll * 16 * kStageRow +
+    const int64_t grid = scan_grid(Lk);
+    if (with_hist && scan_list_cap(Lk) >= 65536) return hipErrorInvalidValue;
+    if (lists.keys) lists.cap = scan_list_cap(Lk);
+    const size_t lds = scan_lds_bytes(Lk, T, lists.keys != nullptr) +
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
     switch (T) {
 #define DSA_SCAN_CASE(n) \
-  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, dim3((unsigned)grid), dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, ngroups, ctr, with_hist); break;
+  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, dim3((unsigned)grid), dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists); break;
       DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
       DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
 #undef DSA_SCAN_CASE

@@ -11,12 +11,27 @@ constexpr int kDecodeTMax = 8;            // streaming-scan limit of the indexer
 constexpr int kScanHistTMax = 4;          // the scan also builds the top-k histogram up to here
 constexpr int kTopkMultiRowsMax = 8;      // rows handled by the multi-block top-k
 
+constexpr int kListM = 32;                // per-workgroup local top list of the decode scan
+
 // ---- index scores
+// Per-workgroup local top lists of the decode scan.  Entry j of workgroup b's
+// list for row t sits at [(t * kListM + j) * scan_grid + b]; entries are in
+// (score desc, index asc) order, unused entries have key 0.
+struct ScanLists {
+  uint32_t* keys = nullptr;    // [T][kListM][scan_grid] order keys
+  uint32_t* idx = nullptr;     // [T][kListM][scan_grid] key indices
+  uint32_t* count = nullptr;   // [T][scan_grid] kept | (more than kListM visible) << 31
+  int cap = 0;                 // local positions per workgroup (set by the launcher)
+};
+int scan_grid(int64_t Lk);     // workgroups of the decode scan
+int scan_list_cap(int64_t Lk); // scores a scan workgroup keeps in LDS per row
+size_t scan_lds_bytes(int64_t Lk, int T, bool lists);   // dynamic LDS of the decode scan
 // topk_counters: optional workspace counter region; when given (T <=
-// kScanHistTMax) the scan also builds the top-k's level-1 histogram there
+// kScanHistTMax) the scan also builds the top-k's level-1 histogram there.
+// lists: optional per-workgroup local top lists (exclusive with the histogram).
 hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                                int64_t Lk, int T, float* scores, int64_t ld, hipStream_t st,
-                               void* topk_counters = nullptr);
+                               void* topk_counters = nullptr, ScanLists lists = ScanLists{});
 
 // ---- top-k
 size_t topk_scratch_bytes(int64_t Lk, int T, int k);
@@ -47,6 +62,26 @@ struct AttnArgs {
 size_t attn_scratch_bytes(int T, int k_len, int hkv);
 hipError_t launch_sparse_attn(const AttnArgs& a, void* scratch, hipStream_t st);
 hipError_t launch_swa_attn(const AttnArgs& a, void* scratch, hipStream_t st);
+
+// ---- fused decode tail: selection from the scan's lists + attention + merge
+struct DecodeArgs {
+  AttnArgs a;                  // q, k, v, n_rows = Lk, T, sink, sm_scale, out, lse
+  const float* scores;         // [T][ld] (re-selection when the lists may miss a winner)
+  int64_t ld;
+  int64_t Lk;
+  int k;
+  const uint32_t* lkeys;       // scan lists (ScanLists layout)
+  const uint32_t* lidx;
+  const uint32_t* lcount;
+  int nlists;                  // scan workgroups
+  int32_t* idx_out;            // [T][k] or null
+  float* part;                 // [T][4][n_chunks] partials
+  uint32_t* unit_ctr;          // [T][4], zero between calls (counter region)
+  int n_chunks;
+};
+constexpr size_t kUnitCtrOffset = size_t(3) << 20;   // inside the counter region
+int decode_chunks(int k);
+hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 
 // ---- workspace
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

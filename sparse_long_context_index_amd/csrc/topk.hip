@@ -27,6 +27,7 @@
 // the scores row itself (same result, slower).
 #include "dsa_common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
@@ -41,67 +42,6 @@ constexpr int kCandCap = 16384;                                 // LDS candidate
 constexpr int kHistRange = 2048;                                // per hist block
 constexpr int kRowThreads = 1024;
 constexpr int kRowCap = 6144;                                   // LDS candidates per row
-
-// ------------------------------------------------------------ block helpers
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm[wv] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    uint32_t s = sm[i];
-    base += (i < wv) ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
-// Largest bin b with suffix(b) = sum_{b' >= b} hist[b'] >= need (need >= 1 and
-// the histogram total >= need).  Writes the bin and suffix(b + 1) to *bin and
-// *above (shared).  All threads must call it.
-template <int NT, int NB>
-__device__ void find_threshold_bin(const uint32_t* hist, uint32_t need, uint32_t* scan_sm,
-                                   uint32_t* bin, uint32_t* above) {
-  constexpr int PER = NB >= NT ? NB / NT : 1;
-  static_assert(NB < NT || PER * NT == NB, "bins per thread");
-  const int j = threadIdx.x;
-  const int base = NB - (j + 1) * PER;          // thread 0 owns the top bins
-  const bool owns = base >= 0;                  // threads beyond the bins own none
-  uint32_t h[PER];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    h[i] = owns ? hist[base + i] : 0u;
-    sum += h[i];
-  }
-  uint32_t tot;
-  const uint32_t excl = block_excl_scan<NT>(sum, scan_sm, &tot);
-  if (owns && excl < need && excl + sum >= need) {
-    uint32_t acc = excl;
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (acc + h[i] >= need) {
-        *bin = (uint32_t)(base + i);
-        *above = acc;
-        break;
-      }
-      acc += h[i];
-    }
-  }
-  __syncthreads();
-}
 
 // Sources of candidates for the final pass, walked in ascending index order
 // as nseg() consecutive segments.  get() returns (key, index); key 0 marks an
@@ -425,7 +365,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                                int64_t Lk, int T, int k,
                                                                int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint2 cand[kRowCap];
   __shared__ FinalShared fs;
   __shared__ uint32_t s_b1, s_above1;

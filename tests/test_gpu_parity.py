@@ -330,7 +330,8 @@ def check_decode(d, Lk, T, k, o, idx, S, sink=True):
 
 
 @pytest.mark.parametrize("L,T,k,sink", [(3000, 1, 256, True), (5000, 2, 2048, False), (20000, 4, 2048, True),
-                                        (100, 3, 2048, True), (40000, 8, 512, True), (1, 1, 1, True)])
+                                        (100, 3, 2048, True), (40000, 8, 512, True), (1, 1, 1, True),
+                                        (150000, 2, 2048, True), (66000, 3, 700, False), (262000, 4, 2048, True)])
 def test_decode_step(dev, L, T, k, sink):
     cfg = synth.DecodeConfig("t", L=L, T=T, k=k, plant_frac=0.01, seed=L + T)
     d = synth.decode_inputs(cfg)
@@ -352,3 +353,59 @@ def test_decode_step_deterministic_and_workspace_reuse(dev):
     b = run_decode(dev, d, cfg.Lk, 2, 2048, ws=ws)
     for x, y in zip(a, b):
         assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+# Edge cases of the per-workgroup list selection inside the decode step: a
+# run of near-equal winners that overflows some workgroups' lists (forcing the
+# full-row re-selection), the same run spread thinly enough that no list
+# overflows, scores that all tie, a single attention chunk, and a long
+# four-row step that takes the histogram top-k instead of the lists.
+
+def clustered_inputs(L, T, c0, c1, seed):
+    cfg = synth.DecodeConfig("c", L=L, T=T, k=2048, plant_frac=0.0, seed=seed)
+    d = synth.decode_inputs(cfg)
+    S = oracle.index_scores(d["q_idx"], d["w"], d["k_idx"], cfg.Lk, T)
+    best = int(np.argmax(S[0, :cfg.Lk - T + 1]))
+    rows = np.repeat(d["k_idx"][best][None], c1 - c0, axis=0)
+    flip = np.random.default_rng(seed).integers(0, 2, size=rows.shape).astype(np.uint8)
+    flip[(rows & 0x7F) >= 0x7E] = 0                  # never step onto a NaN code
+    d["k_idx"] = d["k_idx"].copy()
+    d["k_idx"][c0:c1] = rows ^ flip
+    return d, cfg.Lk
+
+
+@pytest.mark.parametrize("L,T,c0,c1", [(40000, 2, 10001, 13001), (300000, 1, 123457, 126457),
+                                       (300000, 1, 299000, 300001)])
+def test_decode_step_clustered_winners(dev, L, T, c0, c1):
+    d, Lk = clustered_inputs(L, T, c0, c1, seed=L + c0)
+    o, idx, S, _ = run_decode(dev, d, Lk, T, 2048)
+    check_decode(d, Lk, T, 2048, o, idx, S)
+
+
+@pytest.mark.parametrize("L,T,k", [(20000, 2, 2048), (70000, 1, 1000), (2500, 3, 2048)])
+def test_decode_step_all_scores_tie(dev, L, T, k):
+    cfg = synth.DecodeConfig("z", L=L, T=T, k=k, plant_frac=0.0, seed=L)
+    d = synth.decode_inputs(cfg)
+    d["q_idx"] = np.zeros_like(d["q_idx"])          # every score is zero
+    o, idx, S, _ = run_decode(dev, d, cfg.Lk, T, k)
+    assert np.all(S[:, :cfg.Lk - T + 1] == 0)
+    for t in range(T):
+        n = min(k, cfg.Lk - T + t + 1)
+        assert np.array_equal(idx[t, :n], np.arange(n))
+    check_decode(d, cfg.Lk, T, k, o, idx, S)
+
+
+@pytest.mark.parametrize("L,T,k", [(9000, 1, 100), (9000, 2, 128), (60000, 1, 129)])
+def test_decode_step_chunk_edges(dev, L, T, k):
+    cfg = synth.DecodeConfig("e", L=L, T=T, k=k, plant_frac=0.01, seed=L + k)
+    d = synth.decode_inputs(cfg)
+    o, idx, S, _ = run_decode(dev, d, cfg.Lk, T, k)
+    check_decode(d, cfg.Lk, T, k, o, idx, S)
+
+
+@pytest.mark.timeout(600)
+def test_decode_step_long_four_rows(dev):
+    cfg = synth.DecodeConfig("h", L=1000000, T=4, k=2048, plant_frac=0.002, seed=77)
+    d = synth.decode_inputs(cfg)
+    o, idx, S, _ = run_decode(dev, d, cfg.Lk, 4, 2048)
+    check_decode(d, cfg.Lk, 4, 2048, o, idx, S)
