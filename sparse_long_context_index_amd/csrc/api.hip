@@ -236,9 +236,10 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
     d.lkeys = sl.keys; d.lidx = sl.idx; d.lcount = sl.count; d.nlists = scan_grid(Lk);
     d.idx_out = idx_out;
     d.part = reinterpret_cast<float*>(base + L.part);
-    d.unit_ctr = reinterpret_cast<uint32_t*>(base + kUnitCtrOffset);
     d.n_chunks = decode_chunks(k);
-    return hip_status(launch_decode_attend(d, st));
+    e = launch_decode_attend(d, st);
+    if (e != hipSuccess || d.n_chunks == 1) return hip_status(e);
+    return hip_status(launch_attn_merge(d.a, d.n_chunks, d.part, st));
   }
   // up to kScanHistTMax tokens the scan also builds the top-k's level-1 histogram
   const bool fused = T <= kScanHistTMax && topk_multi_block(Lk, T);

@@ -130,6 +130,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* scratch, hipStream_t st) 
   return hipGetLastError();
 }
 
+hipError_t launch_attn_merge(const AttnArgs& a, int n_chunks, const float* part, hipStream_t st) {
+  if (n_chunks < 1 || n_chunks > kMaxChunks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS>), dim3(64, a.T), dim3(128), 0, st, a, n_chunks, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_swa_attn(const AttnArgs& a, void* scratch, hipStream_t st) {
   (void)scratch;
   const int chunk = (int)cdiv(a.window, kTileKeys) * kTileKeys;

@@ -105,13 +105,56 @@ constexpr int kStageRow = 144;                     // padded LDS bytes per 128-b
 
 constexpr int kCandCap = 256;                      // candidates ranked directly in the list epilogue
 
+constexpr int kLaneMax = 16;                       // positions per lane of the fast list epilogue
+constexpr int kWaveCand = 64;                      // candidates per wave of the fast list epilogue
+
 struct ListShared {
   RadixShared rs;
   alignas(16) uint32_t key[kCandCap];
   alignas(16) uint32_t idx[kCandCap];
+  alignas(16) uint32_t wk[4][kWaveCand];           // fast path: candidates of each wave
+  alignas(16) uint32_t wi[4][kWaveCand];
+  alignas(16) uint32_t sk[4][kListM];              // fast path: sorted top kListM of each wave
+  alignas(16) uint32_t si[4][kListM];
   uint32_t n;
   uint32_t red[4];
 };
+
+// The largest x such that at least r of the wave's 64 lane values are >= x,
+// i.e. the r-th largest lane value (r >= 1), found bit by bit with ballots.
+__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t v, int r) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t tr = x | (1u << bit);
+    if (__popcll(__ballot(v >= tr)) >= r) x = tr;
+  }
+  return x;
+}
+
+// (kj, ij) precedes (key, id) in (key desc, index asc) order
+__device__ __forceinline__ uint32_t precedes(uint32_t kj, uint32_t ij, uint32_t key, uint32_t id) {
+  return (uint32_t)(kj > key) | ((uint32_t)(kj == key) & (uint32_t)(ij < id));
+}
+
+// count of the N entries (16-byte aligned) preceding (key, id); all reads are
+// issued before the comparisons
+template <int N>
+__device__ __forceinline__ uint32_t count_preceding(const uint32_t* ks, const uint32_t* is, uint32_t key,
+                                                    uint32_t id) {
+  uint4 k4[N / 4], i4[N / 4];
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    k4[q] = *reinterpret_cast<const uint4*>(ks + 4 * q);
+    i4[q] = *reinterpret_cast<const uint4*>(is + 4 * q);
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q)
+    c += precedes(k4[q].x, i4[q].x, key, id) + precedes(k4[q].y, i4[q].y, key, id) +
+         precedes(k4[q].z, i4[q].z, key, id) + precedes(k4[q].w, i4[q].w, key, id);
+  return c;
+}
 
 template <int T>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
@@ -121,7 +164,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
-  float* lsc = reinterpret_cast<float*>(smem + 4 * kScanUnroll * 16 * kStageRow);           // [T][cap]
+  uint32_t* lsk = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);    // [T][cap] order keys
   __shared__ uint32_t red_sm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -176,7 +219,15 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int64_t tile = tile_of(iter, u);
-      if (tile >= ntiles) continue;                             // wave-uniform
+      const int lpos = (iter * 4 * kScanUnroll + wave * kScanUnroll + u) * 16 + col;   // local position
+      if (tile >= ntiles) {                                     // wave-uniform
+        if (lists.keys) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            if ((t & 3) == grp) lsk[t * lists.cap + lpos] = 0u;
+        }
+        continue;
+      }
       const int64_t key = tile * 16 + col;
       const uint8_t* rp = st + (u * 16 + col) * kStageRow + 32 * grp;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(rp);
@@ -195,12 +246,16 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         s[t] = relu_weighted_sum(c, wv[t]);
         if (key > Lk - T + t) s[t] = -INFINITY;       // causal: beyond p_t
       }
+      if (lists.keys) {                                         // keys of the list epilogue; 0: not visible
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          if ((t & 3) == grp) lsk[t * lists.cap + lpos] = key <= Lk - T + t ? order_key(s[t]) : 0u;
+      }
       if (key < Lk) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
           if ((t & 3) == grp) {
             scores[(int64_t)t * ld + key] = s[t];
-            if (lists.keys) lsc[t * lists.cap + (iter * 4 * kScanUnroll + wave * kScanUnroll + u) * 16 + col] = s[t];
             if (with_hist && key <= Lk - T + t) {
               const uint32_t bin = order_key(s[t]) >> 20;
               atomicAdd(&lhist[t * (kHistBins / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -228,114 +283,191 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     auto gidx = [&](int i) -> uint32_t { return (bx + G32 * ((uint32_t)i >> 4)) * 16u + ((uint32_t)i & 15u); };
     for (int t = 0; t < T; ++t) {
       const uint32_t P = (uint32_t)(Lk - T + t + 1);            // keys visible to row t
-      const float* lt = lsc + t * lists.cap;
-      auto key_at = [&](int i) -> uint32_t { return gidx(i) < P ? order_key(lt[i]) : 0u; };
+      const uint32_t* lt = lsk + t * lists.cap;
+      auto key_at = [&](int i) -> uint32_t { return lt[i]; };   // 0 beyond the row's visible keys
       // visible keys of this workgroup: whole tiles below P / 16, plus the partial one
       const uint32_t F = P >> 4, rem = P & 15u;
       uint32_t n_vis = F > bx ? (F - bx + G32 - 1) / G32 * 16u : 0u;
       if (rem && F >= bx && (F - bx) % G32 == 0) n_vis += rem;
       const bool full = n_vis > (uint32_t)kListM;
-      // Candidates are the visible keys >= L0, a lower bound of the kListM-th
-      // largest: the smallest of the maxima of 32 groups of 8 threads (each
-      // group holds a key at least that large).  They are ranked directly
-      // when few; otherwise a radix descent finds the threshold first.
-      uint32_t L0 = 1u;                                         // key 0: not visible
-      if (full) {
+      // Fast path: each wave finds the sorted top kListM of its quarter of the
+      // positions -- its candidates are the keys >= the kListM-th largest of
+      // its lanes' maxima (kListM lanes hold a key at least that large), and
+      // they are ranked directly -- and the four wave lists are merged by rank.  A wave with too many candidates sends the
+      // row to the general path below.
+      const int per_lane = n_loc / 256;
+      bool slow = true;
+      const uint32_t kept = n_vis < (uint32_t)kListM ? n_vis : (uint32_t)kListM;
+      if (per_lane <= kLaneMax) {
+        const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int wbase = wv * (n_loc / 4);
+        uint32_t kk[kLaneMax];
         uint32_t mx = 0;
-        for (int i = threadIdx.x; i < n_loc; i += 256) {
-          const uint32_t kk = key_at(i);
-          mx = mx > kk ? mx : kk;
-        }
 #pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-          const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, 64);
-          mx = mx > y ? mx : y;
+        for (int m = 0; m < kLaneMax; ++m) {
+          const int pos = m < per_lane ? wbase + lane + 64 * m : wbase + lane;   // stays in the row
+          const uint32_t kv = key_at(pos);
+          kk[m] = m < per_lane ? kv : 0u;
+          mx = mx > kk[m] ? mx : kk[m];
         }
-        const uint32_t wmin = wave_incl_minmax<false>(mx);
-        if ((threadIdx.x & 63) == 63) ls.red[threadIdx.x >> 6] = wmin;
-        __syncthreads();
-        uint32_t g = ls.red[0];
+        uint32_t L0w = wave_rth_largest(mx, kListM);
+        L0w = L0w > 1u ? L0w : 1u;                              // key 0: not visible
+        uint32_t* wk = ls.wk[wv];
+        uint32_t* wi = ls.wi[wv];
+        const uint64_t below = (1ull << lane) - 1ull;
+        uint32_t cw = 0;
 #pragma unroll
-        for (int w = 1; w < 4; ++w) g = g < ls.red[w] ? g : ls.red[w];
-        L0 = g > 1u ? g : 1u;
-      }
-      if (threadIdx.x == 0) ls.n = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < n_loc; i += 256) {          // n_loc is a multiple of 256
-        const uint32_t key = key_at(i);
-        const bool pass = key >= L0;
-        const uint64_t m = __ballot(pass);
-        uint32_t base = 0;
-        if ((threadIdx.x & 63) == 0 && m) base = atomicAdd(&ls.n, (uint32_t)__popcll(m));
-        base = (uint32_t)__shfl((int)base, 0, 64);
-        const uint32_t p = base + (uint32_t)__popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
-        if (pass && p < (uint32_t)kCandCap) {
-          ls.key[p] = key;
-          ls.idx[p] = gidx(i);
+        for (int m = 0; m < kLaneMax; ++m) {
+          const bool pass = m < per_lane && kk[m] >= L0w;
+          const uint64_t msk = __ballot(pass);
+          const uint32_t p = cw + (uint32_t)__popcll(msk & below);
+          if (pass && p < (uint32_t)kWaveCand) {
+            wk[p] = kk[m];
+            wi[p] = gidx(wbase + lane + 64 * m);
+          }
+          cw += (uint32_t)__popcll(msk);
         }
-      }
-      __syncthreads();
-      const uint32_t C = ls.n;
-      __syncthreads();
-      if (C > (uint32_t)kCandCap) {
-        // many candidates: exact threshold by radix descent, then collect the kListM kept
-        uint32_t tau = 0, tau2 = 0, r, eq;
-        bool split = false;
-        radix_threshold<256>(key_at, n_loc, (uint32_t)kListM, ls.rs, &tau, &r, &eq);
-        if (eq > r) {                 // keep the r lowest key indices among the ties
-          uint32_t r2, eq2;
-          radix_threshold<256>([&](int i) { return key_at(i) == tau ? ~gidx(i) : 0u; }, n_loc, r, ls.rs, &tau2,
-                               &r2, &eq2);
-          split = true;
+        const uint32_t nw = cw < (uint32_t)kWaveCand ? cw : (uint32_t)kWaveCand;
+        if ((uint32_t)lane >= nw) {                             // pad: key 0 ranks below every candidate
+          wk[lane] = 0u;
+          wi[lane] = 0xFFFFFFFFu;
         }
-        if (threadIdx.x == 0) ls.n = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < n_loc; i += 256) {
-          const uint32_t key = key_at(i);
-          if (key > tau || (key == tau && (!split || ~gidx(i) >= tau2))) {
-            const uint32_t p = atomicAdd(&ls.n, 1u);
-            if (p < (uint32_t)kListM) {
-              ls.key[p] = key;
-              ls.idx[p] = gidx(i);
+        if (lane < kListM) {
+          ls.sk[wv][lane] = 0u;
+          ls.si[wv][lane] = 0xFFFFFFFFu;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if ((uint32_t)lane < nw) {
+          const uint32_t key = wk[lane], id = wi[lane];
+          const uint32_t rank = count_preceding<kWaveCand>(wk, wi, key, id);
+          if (rank < (uint32_t)kListM) {
+            ls.sk[wv][rank] = key;
+            ls.si[wv][rank] = id;
+          }
+        }
+        slow = __syncthreads_or(cw > (uint32_t)kWaveCand);
+        if (!slow && threadIdx.x < 4 * kListM) {
+          const int w = threadIdx.x / kListM, r = threadIdx.x % kListM;
+          const uint32_t key = ls.sk[w][r], id = ls.si[w][r];
+          if (key != 0u) {
+            uint32_t rank = (uint32_t)r;
+#pragma unroll
+            for (int o = 1; o < 4; ++o) {
+              const int w2 = (w + o) & 3;
+              rank += count_preceding<kListM>(ls.sk[w2], ls.si[w2], key, id);
+            }
+            if (rank < (uint32_t)kListM) {
+              const size_t off = ((size_t)t * kListM + rank) * G32 + bx;
+              lists.keys[off] = key;
+              lists.idx[off] = id;
             }
           }
         }
-        __syncthreads();
       }
-      const uint32_t nc = C > (uint32_t)kCandCap ? (ls.n < (uint32_t)kListM ? ls.n : (uint32_t)kListM) : C;
-      const uint32_t kept = nc < (uint32_t)kListM ? nc : (uint32_t)kListM;
-      // rank in (key desc, index asc) order; the first kListM ranks form the
-      // list.  The candidate arrays are padded to a multiple of 16 with key 0,
-      // which ranks below every candidate, so the reads go 16 at a time.
-      const uint32_t ncp = (nc + 15u) & ~15u;
-      if (threadIdx.x >= nc && threadIdx.x < ncp) {
-        ls.key[threadIdx.x] = 0u;
-        ls.idx[threadIdx.x] = 0xFFFFFFFFu;
-      }
-      __syncthreads();
-      if (threadIdx.x < nc) {
-        const uint32_t key = ls.key[threadIdx.x], id = ls.idx[threadIdx.x];
-        uint32_t rank = 0;
-        for (uint32_t j0 = 0; j0 < ncp; j0 += 16) {
-          uint4 k4[4], i4[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            k4[q] = *reinterpret_cast<const uint4*>(&ls.key[j0 + 4 * q]);
-            i4[q] = *reinterpret_cast<const uint4*>(&ls.idx[j0 + 4 * q]);
+      if (slow) {
+        // Candidates are the visible keys >= L0, a lower bound of the kListM-th
+        // largest: the smallest of the maxima of 32 groups of 8 threads (each
+        // group holds a key at least that large).  They are ranked directly
+        // when few; otherwise a radix descent finds the threshold first.
+        uint32_t L0 = 1u;                                         // key 0: not visible
+        if (full) {
+          uint32_t mx = 0;
+          for (int i = threadIdx.x; i < n_loc; i += 256) {
+            const uint32_t kk = key_at(i);
+            mx = mx > kk ? mx : kk;
           }
-          // branch-free: (kj > key) | ((kj == key) & (ij < id))
-          auto before = [&](uint32_t kj, uint32_t ij) {
-            return (uint32_t)(kj > key) | ((uint32_t)(kj == key) & (uint32_t)(ij < id));
-          };
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
-                    before(k4[q].w, i4[q].w);
+          for (int o = 1; o < 8; o <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, 64);
+            mx = mx > y ? mx : y;
+          }
+          const uint32_t wmin = wave_incl_minmax<false>(mx);
+          if ((threadIdx.x & 63) == 63) ls.red[threadIdx.x >> 6] = wmin;
+          __syncthreads();
+          uint32_t g = ls.red[0];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) g = g < ls.red[w] ? g : ls.red[w];
+          L0 = g > 1u ? g : 1u;
         }
-        if (rank < (uint32_t)kListM) {
-          const size_t o = ((size_t)t * kListM + rank) * G32 + bx;
-          lists.keys[o] = key;
-          lists.idx[o] = id;
+        if (threadIdx.x == 0) ls.n = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n_loc; i += 256) {          // n_loc is a multiple of 256
+          const uint32_t key = key_at(i);
+          const bool pass = key >= L0;
+          const uint64_t m = __ballot(pass);
+          uint32_t base = 0;
+          if ((threadIdx.x & 63) == 0 && m) base = atomicAdd(&ls.n, (uint32_t)__popcll(m));
+          base = (uint32_t)__shfl((int)base, 0, 64);
+          const uint32_t p = base + (uint32_t)__popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
+          if (pass && p < (uint32_t)kCandCap) {
+            ls.key[p] = key;
+            ls.idx[p] = gidx(i);
+          }
+        }
+        __syncthreads();
+        const uint32_t C = ls.n;
+        __syncthreads();
+        if (C > (uint32_t)kCandCap) {
+          // many candidates: exact threshold by radix descent, then collect the kListM kept
+          uint32_t tau = 0, tau2 = 0, r, eq;
+          bool split = false;
+          radix_threshold<256>(key_at, n_loc, (uint32_t)kListM, ls.rs, &tau, &r, &eq);
+          if (eq > r) {                 // keep the r lowest key indices among the ties
+            uint32_t r2, eq2;
+            radix_threshold<256>([&](int i) { return key_at(i) == tau ? ~gidx(i) : 0u; }, n_loc, r, ls.rs, &tau2,
+                                 &r2, &eq2);
+            split = true;
+          }
+          if (threadIdx.x == 0) ls.n = 0;
+          __syncthreads();
+          for (int i = threadIdx.x; i < n_loc; i += 256) {
+            const uint32_t key = key_at(i);
+            if (key > tau || (key == tau && (!split || ~gidx(i) >= tau2))) {
+              const uint32_t p = atomicAdd(&ls.n, 1u);
+              if (p < (uint32_t)kListM) {
+                ls.key[p] = key;
+                ls.idx[p] = gidx(i);
+              }
+            }
+          }
+          __syncthreads();
+        }
+        const uint32_t nc = C > (uint32_t)kCandCap ? (ls.n < (uint32_t)kListM ? ls.n : (uint32_t)kListM) : C;
+        // rank in (key desc, index asc) order; the first kListM ranks form the
+        // list.  The candidate arrays are padded to a multiple of 16 with key 0,
+        // which ranks below every candidate, so the reads go 16 at a time.
+        const uint32_t ncp = (nc + 15u) & ~15u;
+        if (threadIdx.x >= nc && threadIdx.x < ncp) {
+          ls.key[threadIdx.x] = 0u;
+          ls.idx[threadIdx.x] = 0xFFFFFFFFu;
+        }
+        __syncthreads();
+        if (threadIdx.x < nc) {
+          const uint32_t key = ls.key[threadIdx.x], id = ls.idx[threadIdx.x];
+          uint32_t rank = 0;
+          for (uint32_t j0 = 0; j0 < ncp; j0 += 16) {
+            uint4 k4[4], i4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              k4[q] = *reinterpret_cast<const uint4*>(&ls.key[j0 + 4 * q]);
+              i4[q] = *reinterpret_cast<const uint4*>(&ls.idx[j0 + 4 * q]);
+            }
+            // branch-free: (kj > key) | ((kj == key) & (ij < id))
+            auto before = [&](uint32_t kj, uint32_t ij) {
+              return (uint32_t)(kj > key) | ((uint32_t)(kj == key) & (uint32_t)(ij < id));
+            };
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
+                      before(k4[q].w, i4[q].w);
+          }
+          if (rank < (uint32_t)kListM) {
+            const size_t o = ((size_t)t * kListM + rank) * G32 + bx;
+            lists.keys[o] = key;
+            lists.idx[o] = id;
+          }
         }
       }
       if (threadIdx.x >= kept && threadIdx.x < kListM) {       // unused entries

@@ -62,8 +62,11 @@ struct AttnArgs {
 size_t attn_scratch_bytes(int T, int k_len, int hkv);
 hipError_t launch_sparse_attn(const AttnArgs& a, void* scratch, hipStream_t st);
 hipError_t launch_swa_attn(const AttnArgs& a, void* scratch, hipStream_t st);
+// merge of per-chunk partials [(t * 4 + g) * n_chunks + c] of the GQA-4 attention, with the sink
+hipError_t launch_attn_merge(const AttnArgs& a, int n_chunks, const float* part, hipStream_t st);
 
-// ---- fused decode tail: selection from the scan's lists + attention + merge
+// ---- fused decode tail: selection from the scan's lists + attention (partials
+// merged by launch_attn_merge when there is more than one chunk)
 struct DecodeArgs {
   AttnArgs a;                  // q, k, v, n_rows = Lk, T, sink, sm_scale, out, lse
   const float* scores;         // [T][ld] (re-selection when the lists may miss a winner)
@@ -76,10 +79,8 @@ struct DecodeArgs {
   int nlists;                  // scan workgroups
   int32_t* idx_out;            // [T][k] or null
   float* part;                 // [T][4][n_chunks] partials
-  uint32_t* unit_ctr;          // [T][4], zero between calls (counter region)
   int n_chunks;
 };
-constexpr size_t kUnitCtrOffset = size_t(3) << 20;   // inside the counter region
 int decode_chunks(int k);
 hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 
