@@ -43,12 +43,16 @@ struct Window {
   }
 };
 
-template <int HKV, int NW, class Src>
+// NTB: threads of the workgroup (at least NW waves); waves beyond NW only take
+// part in the barriers.
+template <int HKV, int NW, class Src, int NTB = NW * 64>
 __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, int t, int g, int c, int n_chunks,
                              int p0, int p1, float* part, char* smem) {
   constexpr int GH = 64 / HKV;              // query heads per KV head
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const bool wave_on = wave < NW;
+  static_assert(NTB >= NW * 64 && NTB % 64 == 0, "workgroup shape");
   const int col = lane & 15;
   const int kg = lane >> 4;
   const float qscale = a.sm_scale * kLog2e;
@@ -79,7 +83,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
 
   for (int rd = 0; rd < rounds; ++rd) {
     const int tile = rd * NW + wave;
-    const bool active = tile < ntiles;       // wave-uniform
+    const bool active = wave_on && tile < ntiles;   // wave-uniform
     const int tb = p0 + tile * kTileKeys;
     bf16x8 pf;
     if (active) {
@@ -183,15 +187,18 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
   float* lw = mw + NW * 16;                                 // [NW][16]
   float* ow = lw + NW * 16;                                 // [NW][16][128]
   __syncthreads();                                          // V staging is dead
-  if (lane < 16) {
-    mw[wave * 16 + lane] = m;
-    lw[wave * 16 + lane] = lsum;
+  if (wave_on) {
+    if (lane < 16) {
+      mw[wave * 16 + lane] = m;
+      lw[wave * 16 + lane] = lsum;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ow[(wave * 16 + 4 * kg + i) * 128 + blk * 16 + col] = o[blk][i];
   }
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ow[(wave * 16 + 4 * kg + i) * 128 + blk * 16 + col] = o[blk][i];
   __syncthreads();
+  if (threadIdx.x >= NW * 64) return;
 
   // every thread combines outputs (head hc, dim dv) for hc = h0 + R*q; all
   // LDS reads are issued before any result is written

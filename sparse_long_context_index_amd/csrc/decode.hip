@@ -6,26 +6,26 @@
 // The decode scan leaves, for every query row, one list per scan workgroup
 // holding that workgroup's exact local top-32 keys sorted by (score desc,
 // index asc), with a flag when more than 32 of its keys were visible.  Every
-// workgroup of this kernel (512 threads, one list per thread) then,
-// redundantly and without communicating:
-//   1. loads its list's keys and indices into registers;
+// workgroup of this kernel (512 threads, one list each) then, redundantly and
+// without communicating:
+//   1. loads its threads' lists (keys and indices) into registers;
 //   2. finds the k-th entry of the union in (score desc, index asc) order: a
 //      histogram of the keys over the range between a lower bound of the
 //      threshold and the largest key picks the bin that holds it, and the
-//      entries of that bin are ranked directly (a radix descent over the
-//      bin's keys and then indices takes over when the bin is large);
+//      entries of that bin are ranked directly when few (otherwise a radix
+//      descent over the bin's keys, and then over tied indices, finishes);
 //   3. keeps from every list the prefix that precedes that entry, and checks
 //      that the union held the true top-k: when a capped list keeps its last
 //      entry, keys it dropped may belong to the top-k, and only then the
 //      workgroup re-selects from the whole scores row (same result, slower);
-//   4. attends over its chunk of 256 kept keys for one KV head (the same tile
+//   4. attends over its chunk of 128 kept keys for one KV head (the same tile
 //      loop as sparse_gqa_attn) and writes a partial (max, sum, output), or
 //      the output itself when one chunk covers the k keys.
-// The partials are merged with the sink by the attention merge kernel.
-// Every workgroup derives the same kept list in the same order, so the
-// result is deterministic; the list is sorted only for the optional idx
-// output.  The scan deals 16-key tiles round-robin to its workgroups, so a run
-// of up to 2,048 consecutive winners puts at most 16 in any one list.
+// The partials are merged with the sink by the attention merge kernel.  Every
+// workgroup derives the same kept list in the same order, so the result is
+// deterministic; the list is sorted only for the optional idx output.  The
+// scan deals 16-key tiles round-robin to its workgroups, so a run of up to
+// 2,048 consecutive winners puts at most 16 in any one list.
 #include "attn_core.hpp"
 #include "dsa_common.hpp"
 #include "kernels.hpp"
@@ -35,10 +35,11 @@ namespace dsa {
 
 namespace {
 
-constexpr int kDecNW = 8;                          // waves per workgroup
-constexpr int kDecNT = kDecNW * 64;                // threads: one scan list each
+constexpr int kDecNT = 512;                        // threads: one scan list each
+constexpr int kDecNW = 4;                          // attention waves
 constexpr int kDecChunk = kDecNW * kTileKeys;      // kept keys per workgroup
-constexpr int kMaxLists = kDecNT;
+constexpr int kMaxLists = 512;
+constexpr int kLPT = kMaxLists / kDecNT;           // scan lists per thread
 constexpr int kDecMaxChunks = DSA_TOPK_MAX / kDecChunk;
 constexpr int kC1Cap = 64;                         // threshold-bin entries ranked directly
 
@@ -55,7 +56,6 @@ struct DecodeShared {
   };
   int32_t sel[DSA_TOPK_MAX];
   uint32_t scan[32];
-  uint32_t flag;
 };
 
 struct LdsList {
@@ -96,24 +96,36 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
   const int k = d.k;
   const int nl = d.nlists;
 
-  // ---- 1. this thread's list: keys and indices in registers (coalesced over
-  // the threads for every entry), clamped so that every load is in flight at once
-  const int l = tid < nl ? tid : nl - 1;
+  // ---- 1. this thread's lists tid + 512 q: keys and indices in registers
+  // (coalesced over the threads for every entry), clamped so that every load
+  // is in flight at once
   const uint32_t* key_row = d.lkeys + (size_t)t * kListM * nl;
   const uint32_t* idx_row = d.lidx + (size_t)t * kListM * nl;
-  uint32_t w = d.lcount[(size_t)t * nl + l];
-  uint32_t kA[kListM], iA[kListM];
+  uint32_t kA[kLPT][kListM], iA[kLPT][kListM], n[kLPT];
+  bool full[kLPT];
 #pragma unroll
-  for (int j = 0; j < kListM; ++j) {
-    kA[j] = key_row[j * nl + l];
-    iA[j] = idx_row[j * nl + l];
+  for (int q = 0; q < kLPT; ++q) {
+    const int lq = tid + kDecNT * q;
+    const int l = lq < nl ? lq : nl - 1;
+    const uint32_t w = d.lcount[(size_t)t * nl + l];
+#pragma unroll
+    for (int j = 0; j < kListM; ++j) {
+      kA[q][j] = key_row[j * nl + l];
+      iA[q][j] = idx_row[j * nl + l];
+    }
+    n[q] = lq < nl ? w & 0x7FFFFFFFu : 0u;
+    full[q] = lq < nl && (w >> 31) != 0u;
   }
-  if (tid >= nl) w = 0u;
-  const uint32_t n = w & 0x7FFFFFFFu;
-  const bool full = (w >> 31) != 0u;
   uint32_t M;
-  block_excl_scan<kDecNT>(n, sh.scan, &M);
-  const bool any_full = __syncthreads_or(full);
+  uint32_t n_all = 0;
+  bool full_any = false;
+#pragma unroll
+  for (int q = 0; q < kLPT; ++q) {
+    n_all += n[q];
+    full_any |= full[q];
+  }
+  block_excl_scan<kDecNT>(n_all, sh.scan, &M);
+  const bool any_full = __syncthreads_or(full_any);
 
   // ---- 2. the k-th entry (tk, ti) of the union: keep key > tk, or key == tk and index <= ti
   bool fallback;
@@ -131,11 +143,16 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     // over the bins of this range keeps the LDS atomics apart.
     RadixShared& rs = sh.s.rs;
     const uint32_t cth = (uint32_t)((k + nl - 1) / nl);
-    uint32_t kmax = n ? kA[0] : 0u, xc = 0xFFFFFFFFu, xl = 0xFFFFFFFFu, nc = n >= cth ? 1u : 0u;
+    uint32_t kmax = 0u, xc = 0xFFFFFFFFu, xl = 0xFFFFFFFFu, nc = 0u;
 #pragma unroll
-    for (int j = 0; j < kListM; ++j) {
-      if ((uint32_t)j + 1 == cth && n >= cth) xc = kA[j];
-      if ((uint32_t)j + 1 == n) xl = kA[j];
+    for (int q = 0; q < kLPT; ++q) {
+      if (n[q]) kmax = kmax > kA[q][0] ? kmax : kA[q][0];
+      nc += n[q] >= cth;
+#pragma unroll
+      for (int j = 0; j < kListM; ++j) {
+        if ((uint32_t)j + 1 == cth && n[q] >= cth) xc = xc < kA[q][j] ? xc : kA[q][j];
+        if ((uint32_t)j + 1 == n[q]) xl = xl < kA[q][j] ? xl : kA[q][j];
+      }
     }
     block_reduce_mmms<kDecNT>(kmax, xc, xl, nc, sh.scan);
     const uint32_t L0 = (uint64_t)nc * cth >= (uint64_t)k ? xc : xl;
@@ -148,11 +165,13 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       for (int i = tid; i < nbins; i += kDecNT) rs.hist[i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kListM; ++j) {
-        const uint32_t u = kA[j] - L0;
-        if ((uint32_t)j < n && kA[j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
-          atomicAdd(&rs.hist[(u >> shift) & mask], 1u);
-      }
+      for (int q = 0; q < kLPT; ++q)
+#pragma unroll
+        for (int j = 0; j < kListM; ++j) {
+          const uint32_t u = kA[q][j] - L0;
+          if ((uint32_t)j < n[q] && kA[q][j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
+            atomicAdd(&rs.hist[(u >> shift) & mask], 1u);
+        }
       __syncthreads();
     };
     level(s1, 0xFFFu, 32, 0u, kHistBins);
@@ -161,23 +180,28 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     uint32_t need = (uint32_t)k - rs.above;    // entries still to take from bin b1
     const uint32_t cnt1 = rs.hist[b1];
     __syncthreads();
-    auto in_b1 = [&](int j) {
-      return (uint32_t)((uint32_t)j < n) & (uint32_t)(kA[j] >= L0) & (uint32_t)(((kA[j] - L0) >> s1) == b1);
+    auto in_b1 = [&](int q, int j) {
+      return (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] >= L0) &
+             (uint32_t)(((kA[q][j] - L0) >> s1) == b1);
     };
     if (cnt1 <= (uint32_t)kC1Cap) {
       // rank the bin's entries directly; the one of rank need - 1 is the k-th
       uint32_t m = 0;
 #pragma unroll
-      for (int j = 0; j < kListM; ++j) m += in_b1(j);
+      for (int q = 0; q < kLPT; ++q)
+#pragma unroll
+        for (int j = 0; j < kListM; ++j) m += in_b1(q, j);
       uint32_t tot;
       uint32_t p = block_excl_scan<kDecNT>(m, sh.scan, &tot);
 #pragma unroll
-      for (int j = 0; j < kListM; ++j)
-        if (in_b1(j)) {
-          sh.s.ck[p] = kA[j];
-          sh.s.ci[p] = iA[j];
-          ++p;
-        }
+      for (int q = 0; q < kLPT; ++q)
+#pragma unroll
+        for (int j = 0; j < kListM; ++j)
+          if (in_b1(q, j)) {
+            sh.s.ck[p] = kA[q][j];
+            sh.s.ci[p] = iA[q][j];
+            ++p;
+          }
       const uint32_t ncp = (cnt1 + 15u) & ~15u;  // padded with key 0, which ranks below every entry
       if ((uint32_t)tid >= cnt1 && (uint32_t)tid < ncp) {
         sh.s.ck[tid] = 0u;
@@ -240,26 +264,41 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     fallback = false;
   }
 
-  // ---- 3. the kept prefix of this list; a capped list keeping its last entry may hide winners
-  uint32_t cnt = 0;
-  if (!fallback) {
-    if (n_vis <= (int64_t)k) {
-      cnt = n;
-    } else {
+  // ---- 3. the kept prefix of each list; a capped list keeping its last entry may hide winners
+  uint32_t cnt[kLPT];
 #pragma unroll
-      for (int j = 0; j < kListM; ++j)
-        cnt += (uint32_t)((uint32_t)j < n) & ((uint32_t)(kA[j] > tk) | ((uint32_t)(kA[j] == tk) & (uint32_t)(iA[j] <= ti)));
+  for (int q = 0; q < kLPT; ++q) cnt[q] = 0u;
+  if (!fallback) {
+    bool hides = false;
+#pragma unroll
+    for (int q = 0; q < kLPT; ++q) {
+      if (n_vis <= (int64_t)k) {
+        cnt[q] = n[q];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kListM; ++j)
+          cnt[q] += (uint32_t)((uint32_t)j < n[q]) &
+                    ((uint32_t)(kA[q][j] > tk) | ((uint32_t)(kA[q][j] == tk) & (uint32_t)(iA[q][j] <= ti)));
+      }
+      hides |= full[q] && cnt[q] == n[q];
     }
-    fallback = __syncthreads_or(full && cnt == n);
+    fallback = __syncthreads_or(hides);
   }
   __syncthreads();
 
   uint32_t n_sel;
   if (!fallback) {
-    const uint32_t base = block_excl_scan<kDecNT>(cnt, sh.scan, &n_sel);
+    uint32_t cnt_all = 0;
 #pragma unroll
-    for (int j = 0; j < kListM; ++j)
-      if ((uint32_t)j < cnt && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[j];
+    for (int q = 0; q < kLPT; ++q) cnt_all += cnt[q];
+    uint32_t base = block_excl_scan<kDecNT>(cnt_all, sh.scan, &n_sel);
+#pragma unroll
+    for (int q = 0; q < kLPT; ++q) {
+#pragma unroll
+      for (int j = 0; j < kListM; ++j)
+        if ((uint32_t)j < cnt[q] && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[q][j];
+      base += cnt[q];
+    }
     if (n_sel > (uint32_t)DSA_TOPK_MAX) n_sel = DSA_TOPK_MAX;
   } else {
     const float* row = d.scores + (int64_t)t * d.ld;
@@ -285,7 +324,7 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
   const int p0 = c * kDecChunk < (int)n_sel ? c * kDecChunk : (int)n_sel;
   const int p1 = p0 + kDecChunk < (int)n_sel ? p0 + kDecChunk : (int)n_sel;
   LdsList src{sh.sel, a.n_rows};
-  attend_chunk<DSA_KV_HEADS, kDecNW>(a, src, t, g, c, d.n_chunks, p0, p1, d.part, sh.attn);
+  attend_chunk<DSA_KV_HEADS, kDecNW, LdsList, kDecNT>(a, src, t, g, c, d.n_chunks, p0, p1, d.part, sh.attn);
 }
 
 }  // namespace

@@ -156,7 +156,7 @@ __device__ __forceinline__ uint32_t count_preceding(const uint32_t* ks, const ui
   return c;
 }
 
-template <int T>
+template <int T, bool kLists>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       const int64_t tile = tile_of(iter, u);
       const int lpos = (iter * 4 * kScanUnroll + wave * kScanUnroll + u) * 16 + col;   // local position
       if (tile >= ntiles) {                                     // wave-uniform
-        if (lists.keys) {
+        if (kLists) {
 #pragma unroll
           for (int t = 0; t < T; ++t)
             if ((t & 3) == grp) lsk[t * lists.cap + lpos] = 0u;
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         s[t] = relu_weighted_sum(c, wv[t]);
         if (key > Lk - T + t) s[t] = -INFINITY;       // causal: beyond p_t
       }
-      if (lists.keys) {                                         // keys of the list epilogue; 0: not visible
+      if (kLists) {                                             // keys of the list epilogue; 0: not visible
 #pragma unroll
         for (int t = 0; t < T; ++t)
           if ((t & 3) == grp) lsk[t * lists.cap + lpos] = key <= Lk - T + t ? order_key(s[t]) : 0u;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       __syncthreads();
     }
   }
-  if (lists.keys) {
+  if (kLists) {
     __syncthreads();
     ListShared& ls = *reinterpret_cast<ListShared*>(smem + 4 * kScanUnroll * 16 * kStageRow +
                                                      (size_t)T * lists.cap * sizeof(float));
@@ -584,9 +584,17 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
     const size_t lds = scan_lds_bytes(Lk, T, lists.keys != nullptr) +
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const bool with_lists = lists.keys != nullptr;
     switch (T) {
-#define DSA_SCAN_CASE(n) \
-  case n: hipLaunchKernelGGL(idx_scan_kernel<n>, dim3((unsigned)grid), dim3(256), lds, st, q_idx, w, k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists); break;
+#define DSA_SCAN_CASE(n)                                                                                    \
+  case n:                                                                                                   \
+    if (with_lists)                                                                                         \
+      hipLaunchKernelGGL((idx_scan_kernel<n, true>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,    \
+                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists);                            \
+    else                                                                                                    \
+      hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,   \
+                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists);                            \
+    break;
       DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
       DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
 #undef DSA_SCAN_CASE
