@@ -95,41 +95,109 @@ __device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
 // first digit) with two 16-bit counters per LDS word; the workgroup adds its
 // counts to replica blockIdx.x % kHistReplicas.
 //
-// lists (optional, exclusive with with_hist): the workgroup also keeps its
-// scores in LDS and, at the end, writes for every query row its exact local
-// top-kListM keys as a list sorted by (score desc, index asc) of order keys
-// and key indices, with a count word (bit 31: more than kListM of its keys
-// were visible).  The fused decode step selects the global top-k from
-// these lists.
+// lists (optional, exclusive with with_hist): every wave also keeps, per
+// query row, the running top kListM of the keys it has scored: keys above the
+// wave's threshold are appended to a wave-private LDS buffer, and a buffer
+// that passes kBufTrigger entries is cut back to its exact top kListM, whose
+// smallest key becomes the new threshold (a later key equal to it has a larger
+// index and cannot enter).  At the end the four wave sets are merged by rank
+// into the workgroup's exact top kListM, written as a list sorted by (score
+// desc, index asc) of order keys and key indices, with a count word (bit 31:
+// more than kListM of its keys were visible).  The fused decode step selects
+// the global top-k from these lists.
 constexpr int kStageRow = 144;                     // padded LDS bytes per 128-byte key row
+constexpr int kBufCap = 256;                       // wave buffer entries per row
+constexpr int kBufTrigger = kBufCap - 4 * 16;      // room for one more step of appends
 
-constexpr int kCandCap = 256;                      // candidates ranked directly in the list epilogue
-
-constexpr int kLaneMax = 16;                       // positions per lane of the fast list epilogue
-constexpr int kWaveCand = 64;                      // candidates per wave of the fast list epilogue
-
+template <int T>
 struct ListShared {
-  RadixShared rs;
-  alignas(16) uint32_t key[kCandCap];
-  alignas(16) uint32_t idx[kCandCap];
-  alignas(16) uint32_t wk[4][kWaveCand];           // fast path: candidates of each wave
-  alignas(16) uint32_t wi[4][kWaveCand];
-  alignas(16) uint32_t sk[4][kListM];              // fast path: sorted top kListM of each wave
-  alignas(16) uint32_t si[4][kListM];
-  uint32_t n;
-  uint32_t red[4];
+  alignas(16) uint32_t bk[4][T][kBufCap];          // wave buffers: order keys
+  alignas(16) uint32_t bi[4][T][kBufCap];          // and key indices
+  uint32_t rank[4 * kListM];                       // merge: partial ranks of the wave sets' entries
 };
+static_assert(sizeof(ListShared<1>) == 8 * 4 * kBufCap + 4 * 4 * kListM, "list LDS size");
+static_assert(sizeof(ListShared<4>) == 8 * 4 * 4 * kBufCap + 4 * 4 * kListM, "list LDS size");
 
-// The largest x such that at least r of the wave's 64 lane values are >= x,
-// i.e. the r-th largest lane value (r >= 1), found bit by bit with ballots.
-__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t v, int r) {
-  uint32_t x = 0;
+// Cuts a wave's buffer (n entries, n <= kBufCap) back to its top kListM by
+// (key desc, index asc), in place and in no particular order; returns the
+// new count and sets *theta to the smallest key kept when the buffer was cut.
+// The kListM-th key and, for ties, the kept indices are found bit by bit with
+// ballots over the E entries each lane holds (n <= 64 E).
+template <int E>
+__device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, uint32_t n, uint32_t* theta) {
+  const int lane = threadIdx.x & 63;
+  bool v[E];
+  uint32_t kk[E], ii[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    v[q] = (uint32_t)(lane + 64 * q) < n;
+    kk[q] = bk[lane + 64 * q];
+    ii[q] = bi[lane + 64 * q];
+    if (!v[q]) kk[q] = 0u;
+  }
+  auto count_ge = [&](uint32_t x) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < E; ++q) c += (uint32_t)__popcll(__ballot(v[q] && kk[q] >= x));
+    return c;
+  };
+  uint32_t tau = 0;
 #pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t tr = x | (1u << bit);
-    if (__popcll(__ballot(v >= tr)) >= r) x = tr;
+    const uint32_t tr = tau | (1u << bit);
+    if (count_ge(tr) >= (uint32_t)kListM) tau = tr;
   }
-  return x;
+  const uint32_t above = tau == 0xFFFFFFFFu ? 0u : count_ge(tau + 1u);
+  const uint32_t r = (uint32_t)kListM - above;             // tau-equal entries to keep
+  uint32_t eq = 0;
+#pragma unroll
+  for (int q = 0; q < E; ++q) eq += (uint32_t)__popcll(__ballot(v[q] && kk[q] == tau));
+  uint32_t imax = 0xFFFFFFFFu;                             // keep tau-equal entries with index <= imax
+  if (eq > r) {
+    uint32_t y = 0;                                        // the r-th largest ~index among them
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t tr = y | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int q = 0; q < E; ++q) cnt += (uint32_t)__popcll(__ballot(v[q] && kk[q] == tau && ~ii[q] >= tr));
+      if (cnt >= r) y = tr;
+    }
+    imax = ~y;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool keep[E];
+  uint32_t pos[E];
+  uint32_t base = 0;
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    keep[q] = v[q] && (kk[q] > tau || (kk[q] == tau && ii[q] <= imax));
+    const uint64_t m = __ballot(keep[q]);
+    pos[q] = base + (uint32_t)__popcll(m & below);
+    base += (uint32_t)__popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // all reads above precede the writes below
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < E; ++q)
+    if (keep[q]) {
+      bk[pos[q]] = kk[q];
+      bi[pos[q]] = ii[q];
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  *theta = tau;
+  return (uint32_t)kListM;
+}
+
+// wave_cut_top_e with as few entries per lane as n allows (n is wave-uniform)
+__device__ __forceinline__ uint32_t wave_cut_top(uint32_t* bk, uint32_t* bi, uint32_t n, uint32_t* theta) {
+  const uint32_t nu = __builtin_amdgcn_readfirstlane(n);
+  if (nu <= (uint32_t)kListM) return nu;
+  if (nu <= 64u) return wave_cut_top_e<1>(bk, bi, nu, theta);
+  if (nu <= 128u) return wave_cut_top_e<2>(bk, bi, nu, theta);
+  return wave_cut_top_e<kBufCap / 64>(bk, bi, nu, theta);
 }
 
 // (kj, ij) precedes (key, id) in (key desc, index asc) order
@@ -164,7 +232,10 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
-  uint32_t* lsk = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);    // [T][cap] order keys
+  ListShared<T>& ls = *reinterpret_cast<ListShared<T>*>(smem + 4 * kScanUnroll * 16 * kStageRow);
+  uint32_t bcnt[T], theta[T];                                   // wave buffer fill and threshold per row
+#pragma unroll
+  for (int t = 0; t < T; ++t) bcnt[t] = theta[t] = 0u;
   __shared__ uint32_t red_sm[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -219,15 +290,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int64_t tile = tile_of(iter, u);
-      const int lpos = (iter * 4 * kScanUnroll + wave * kScanUnroll + u) * 16 + col;   // local position
-      if (tile >= ntiles) {                                     // wave-uniform
-        if (kLists) {
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-            if ((t & 3) == grp) lsk[t * lists.cap + lpos] = 0u;
-        }
-        continue;
-      }
+      if (tile >= ntiles) continue;                             // wave-uniform
       const int64_t key = tile * 16 + col;
       const uint8_t* rp = st + (u * 16 + col) * kStageRow + 32 * grp;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(rp);
@@ -246,10 +309,20 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
         s[t] = relu_weighted_sum(c, wv[t]);
         if (key > Lk - T + t) s[t] = -INFINITY;       // causal: beyond p_t
       }
-      if (kLists) {                                             // keys of the list epilogue; 0: not visible
+      if (kLists) {                                             // append the keys above the threshold
+        const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-          if ((t & 3) == grp) lsk[t * lists.cap + lpos] = key <= Lk - T + t ? order_key(s[t]) : 0u;
+        for (int t = 0; t < T; ++t) {
+          const uint32_t kk = ((t & 3) == grp && key <= Lk - T + t) ? order_key(s[t]) : 0u;
+          const bool pass = kk > theta[t];
+          const uint64_t m = __ballot(pass);
+          const uint32_t pos = bcnt[t] + (uint32_t)__popcll(m & below);
+          if (pass) {
+            ls.bk[wave][t][pos] = kk;
+            ls.bi[wave][t][pos] = (uint32_t)key;
+          }
+          bcnt[t] += (uint32_t)__popcll(m);
+        }
       }
       if (key < Lk) {
 #pragma unroll
@@ -263,6 +336,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
           }
       }
     }
+    if (kLists) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (__builtin_amdgcn_readfirstlane(bcnt[t]) > (uint32_t)kBufTrigger)
+          bcnt[t] = wave_cut_top(ls.bk[wave][t], ls.bi[wave][t], bcnt[t], &theta[t]);
+    }
     __builtin_amdgcn_wave_barrier();
   }
   if (with_hist) {
@@ -273,207 +352,47 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     }
   }
   if (kLists) {
+    // each wave's exact top kListM per row, padded with key 0 (ranks below every key)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      uint32_t* bk = ls.bk[wave][t];
+      uint32_t* bi = ls.bi[wave][t];
+      const uint32_t nw = wave_cut_top(bk, bi, bcnt[t], &theta[t]);
+      if ((uint32_t)lane >= nw && lane < kListM) {
+        bk[lane] = 0u;
+        bi[lane] = 0xFFFFFFFFu;
+      }
+    }
     __syncthreads();
-    ListShared& ls = *reinterpret_cast<ListShared*>(smem + 4 * kScanUnroll * 16 * kStageRow +
-                                                     (size_t)T * lists.cap * sizeof(float));
-    // local position i is key (i % 16) of local tile i / 16, i.e. of global
-    // tile bx + G (i / 16); key indices fit 32 bits (Lk < 2^31)
     const uint32_t bx = blockIdx.x, G32 = gridDim.x;
-    const int n_loc = iter * 4 * kScanUnroll * 16;
-    auto gidx = [&](int i) -> uint32_t { return (bx + G32 * ((uint32_t)i >> 4)) * 16u + ((uint32_t)i & 15u); };
+    const int e = threadIdx.x & (4 * kListM - 1);                // entry: wave e / kListM, slot e % kListM
+    const int half = threadIdx.x / (4 * kListM);                 // compares against waves 2 half, 2 half + 1
     for (int t = 0; t < T; ++t) {
       const uint32_t P = (uint32_t)(Lk - T + t + 1);            // keys visible to row t
-      const uint32_t* lt = lsk + t * lists.cap;
-      auto key_at = [&](int i) -> uint32_t { return lt[i]; };   // 0 beyond the row's visible keys
       // visible keys of this workgroup: whole tiles below P / 16, plus the partial one
       const uint32_t F = P >> 4, rem = P & 15u;
       uint32_t n_vis = F > bx ? (F - bx + G32 - 1) / G32 * 16u : 0u;
       if (rem && F >= bx && (F - bx) % G32 == 0) n_vis += rem;
       const bool full = n_vis > (uint32_t)kListM;
-      // Fast path: each wave finds the sorted top kListM of its quarter of the
-      // positions -- its candidates are the keys >= the kListM-th largest of
-      // its lanes' maxima (kListM lanes hold a key at least that large), and
-      // they are ranked directly -- and the four wave lists are merged by rank.  A wave with too many candidates sends the
-      // row to the general path below.
-      const int per_lane = n_loc / 256;
-      bool slow = true;
-      const uint32_t kept = n_vis < (uint32_t)kListM ? n_vis : (uint32_t)kListM;
-      if (per_lane <= kLaneMax) {
-        const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        const int wbase = wv * (n_loc / 4);
-        uint32_t kk[kLaneMax];
-        uint32_t mx = 0;
-#pragma unroll
-        for (int m = 0; m < kLaneMax; ++m) {
-          const int pos = m < per_lane ? wbase + lane + 64 * m : wbase + lane;   // stays in the row
-          const uint32_t kv = key_at(pos);
-          kk[m] = m < per_lane ? kv : 0u;
-          mx = mx > kk[m] ? mx : kk[m];
-        }
-        uint32_t L0w = wave_rth_largest(mx, kListM);
-        L0w = L0w > 1u ? L0w : 1u;                              // key 0: not visible
-        uint32_t* wk = ls.wk[wv];
-        uint32_t* wi = ls.wi[wv];
-        const uint64_t below = (1ull << lane) - 1ull;
-        uint32_t cw = 0;
-#pragma unroll
-        for (int m = 0; m < kLaneMax; ++m) {
-          const bool pass = m < per_lane && kk[m] >= L0w;
-          const uint64_t msk = __ballot(pass);
-          const uint32_t p = cw + (uint32_t)__popcll(msk & below);
-          if (pass && p < (uint32_t)kWaveCand) {
-            wk[p] = kk[m];
-            wi[p] = gidx(wbase + lane + 64 * m);
-          }
-          cw += (uint32_t)__popcll(msk);
-        }
-        const uint32_t nw = cw < (uint32_t)kWaveCand ? cw : (uint32_t)kWaveCand;
-        if ((uint32_t)lane >= nw) {                             // pad: key 0 ranks below every candidate
-          wk[lane] = 0u;
-          wi[lane] = 0xFFFFFFFFu;
-        }
-        if (lane < kListM) {
-          ls.sk[wv][lane] = 0u;
-          ls.si[wv][lane] = 0xFFFFFFFFu;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if ((uint32_t)lane < nw) {
-          const uint32_t key = wk[lane], id = wi[lane];
-          const uint32_t rank = count_preceding<kWaveCand>(wk, wi, key, id);
-          if (rank < (uint32_t)kListM) {
-            ls.sk[wv][rank] = key;
-            ls.si[wv][rank] = id;
-          }
-        }
-        slow = __syncthreads_or(cw > (uint32_t)kWaveCand);
-        if (!slow && threadIdx.x < 4 * kListM) {
-          const int w = threadIdx.x / kListM, r = threadIdx.x % kListM;
-          const uint32_t key = ls.sk[w][r], id = ls.si[w][r];
-          if (key != 0u) {
-            uint32_t rank = (uint32_t)r;
-#pragma unroll
-            for (int o = 1; o < 4; ++o) {
-              const int w2 = (w + o) & 3;
-              rank += count_preceding<kListM>(ls.sk[w2], ls.si[w2], key, id);
-            }
-            if (rank < (uint32_t)kListM) {
-              const size_t off = ((size_t)t * kListM + rank) * G32 + bx;
-              lists.keys[off] = key;
-              lists.idx[off] = id;
-            }
-          }
+      const uint32_t kept = full ? (uint32_t)kListM : n_vis;
+      // merge: the rank of an entry among the 4 kListM entries is the number preceding it
+      const uint32_t key = ls.bk[e / kListM][t][e % kListM], id = ls.bi[e / kListM][t][e % kListM];
+      const uint32_t part = count_preceding<kListM>(ls.bk[2 * half][t], ls.bi[2 * half][t], key, id) +
+                            count_preceding<kListM>(ls.bk[2 * half + 1][t], ls.bi[2 * half + 1][t], key, id);
+      if (half == 1) ls.rank[e] = part;
+      __syncthreads();
+      if (half == 0 && key != 0u) {
+        const uint32_t rank = part + ls.rank[e];
+        if (rank < (uint32_t)kListM) {
+          const size_t off = ((size_t)t * kListM + rank) * G32 + bx;
+          lists.keys[off] = key;
+          lists.idx[off] = id;
         }
       }
-      if (slow) {
-        // Candidates are the visible keys >= L0, a lower bound of the kListM-th
-        // largest: the smallest of the maxima of 32 groups of 8 threads (each
-        // group holds a key at least that large).  They are ranked directly
-        // when few; otherwise a radix descent finds the threshold first.
-        uint32_t L0 = 1u;                                         // key 0: not visible
-        if (full) {
-          uint32_t mx = 0;
-          for (int i = threadIdx.x; i < n_loc; i += 256) {
-            const uint32_t kk = key_at(i);
-            mx = mx > kk ? mx : kk;
-          }
-#pragma unroll
-          for (int o = 1; o < 8; o <<= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, 64);
-            mx = mx > y ? mx : y;
-          }
-          const uint32_t wmin = wave_incl_minmax<false>(mx);
-          if ((threadIdx.x & 63) == 63) ls.red[threadIdx.x >> 6] = wmin;
-          __syncthreads();
-          uint32_t g = ls.red[0];
-#pragma unroll
-          for (int w = 1; w < 4; ++w) g = g < ls.red[w] ? g : ls.red[w];
-          L0 = g > 1u ? g : 1u;
-        }
-        if (threadIdx.x == 0) ls.n = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < n_loc; i += 256) {          // n_loc is a multiple of 256
-          const uint32_t key = key_at(i);
-          const bool pass = key >= L0;
-          const uint64_t m = __ballot(pass);
-          uint32_t base = 0;
-          if ((threadIdx.x & 63) == 0 && m) base = atomicAdd(&ls.n, (uint32_t)__popcll(m));
-          base = (uint32_t)__shfl((int)base, 0, 64);
-          const uint32_t p = base + (uint32_t)__popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
-          if (pass && p < (uint32_t)kCandCap) {
-            ls.key[p] = key;
-            ls.idx[p] = gidx(i);
-          }
-        }
-        __syncthreads();
-        const uint32_t C = ls.n;
-        __syncthreads();
-        if (C > (uint32_t)kCandCap) {
-          // many candidates: exact threshold by radix descent, then collect the kListM kept
-          uint32_t tau = 0, tau2 = 0, r, eq;
-          bool split = false;
-          radix_threshold<256>(key_at, n_loc, (uint32_t)kListM, ls.rs, &tau, &r, &eq);
-          if (eq > r) {                 // keep the r lowest key indices among the ties
-            uint32_t r2, eq2;
-            radix_threshold<256>([&](int i) { return key_at(i) == tau ? ~gidx(i) : 0u; }, n_loc, r, ls.rs, &tau2,
-                                 &r2, &eq2);
-            split = true;
-          }
-          if (threadIdx.x == 0) ls.n = 0;
-          __syncthreads();
-          for (int i = threadIdx.x; i < n_loc; i += 256) {
-            const uint32_t key = key_at(i);
-            if (key > tau || (key == tau && (!split || ~gidx(i) >= tau2))) {
-              const uint32_t p = atomicAdd(&ls.n, 1u);
-              if (p < (uint32_t)kListM) {
-                ls.key[p] = key;
-                ls.idx[p] = gidx(i);
-              }
-            }
-          }
-          __syncthreads();
-        }
-        const uint32_t nc = C > (uint32_t)kCandCap ? (ls.n < (uint32_t)kListM ? ls.n : (uint32_t)kListM) : C;
-        // rank in (key desc, index asc) order; the first kListM ranks form the
-        // list.  The candidate arrays are padded to a multiple of 16 with key 0,
-        // which ranks below every candidate, so the reads go 16 at a time.
-        const uint32_t ncp = (nc + 15u) & ~15u;
-        if (threadIdx.x >= nc && threadIdx.x < ncp) {
-          ls.key[threadIdx.x] = 0u;
-          ls.idx[threadIdx.x] = 0xFFFFFFFFu;
-        }
-        __syncthreads();
-        if (threadIdx.x < nc) {
-          const uint32_t key = ls.key[threadIdx.x], id = ls.idx[threadIdx.x];
-          uint32_t rank = 0;
-          for (uint32_t j0 = 0; j0 < ncp; j0 += 16) {
-            uint4 k4[4], i4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              k4[q] = *reinterpret_cast<const uint4*>(&ls.key[j0 + 4 * q]);
-              i4[q] = *reinterpret_cast<const uint4*>(&ls.idx[j0 + 4 * q]);
-            }
-            // branch-free: (kj > key) | ((kj == key) & (ij < id))
-            auto before = [&](uint32_t kj, uint32_t ij) {
-              return (uint32_t)(kj > key) | ((uint32_t)(kj == key) & (uint32_t)(ij < id));
-            };
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
-                      before(k4[q].w, i4[q].w);
-          }
-          if (rank < (uint32_t)kListM) {
-            const size_t o = ((size_t)t * kListM + rank) * G32 + bx;
-            lists.keys[o] = key;
-            lists.idx[o] = id;
-          }
-        }
-      }
-      if (threadIdx.x >= kept && threadIdx.x < kListM) {       // unused entries
-        const size_t o = ((size_t)t * kListM + threadIdx.x) * G32 + bx;
-        lists.keys[o] = 0u;
-        lists.idx[o] = 0xFFFFFFFFu;
+      if (threadIdx.x >= kept && threadIdx.x < kListM) {         // unused entries
+        const size_t off = ((size_t)t * kListM + threadIdx.x) * G32 + bx;
+        lists.keys[off] = 0u;
+        lists.idx[off] = 0xFFFFFFFFu;
       }
       if (threadIdx.x == 0) lists.count[(size_t)t * G32 + bx] = kept | (full ? 0x80000000u : 0u);
       __syncthreads();
@@ -563,8 +482,9 @@ int scan_list_cap(int64_t Lk) {
 }
 
 size_t scan_lds_bytes(int64_t Lk, int T, bool lists) {
+  (void)Lk;
   return (size_t)4 * kScanUnroll * 16 * kStageRow +
-         (lists ? (size_t)T * scan_list_cap(Lk) * sizeof(float) + sizeof(ListShared) : 0);
+         (lists ? (size_t)8 * 4 * T * kBufCap + sizeof(uint32_t) * 4 * kListM : 0);
 }
 
 hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -580,7 +500,6 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
     // 16-bit histogram counters: a workgroup must see fewer than 65536 keys
     const int64_t grid = scan_grid(Lk);
     if (with_hist && scan_list_cap(Lk) >= 65536) return hipErrorInvalidValue;
-    if (lists.keys) lists.cap = scan_list_cap(Lk);
     const size_t lds = scan_lds_bytes(Lk, T, lists.keys != nullptr) +
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;

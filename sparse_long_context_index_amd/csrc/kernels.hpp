@@ -21,10 +21,9 @@ struct ScanLists {
   uint32_t* keys = nullptr;    // [T][kListM][scan_grid] order keys
   uint32_t* idx = nullptr;     // [T][kListM][scan_grid] key indices
   uint32_t* count = nullptr;   // [T][scan_grid] kept | (more than kListM visible) << 31
-  int cap = 0;                 // local positions per workgroup (set by the launcher)
 };
 int scan_grid(int64_t Lk);     // workgroups of the decode scan
-int scan_list_cap(int64_t Lk); // scores a scan workgroup keeps in LDS per row
+int scan_list_cap(int64_t Lk); // keys a scan workgroup scores per row (at most)
 size_t scan_lds_bytes(int64_t Lk, int T, bool lists);   // dynamic LDS of the decode scan
 // topk_counters: optional workspace counter region; when given (T <=
 // kScanHistTMax) the scan also builds the top-k's level-1 histogram there.
