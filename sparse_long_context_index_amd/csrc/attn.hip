@@ -57,30 +57,31 @@ __global__ __launch_bounds__(NW * 64) void swa_attn_kernel(AttnArgs a, int n_chu
 // issued before any is used
 constexpr int kMaxChunks = 32;
 
-template <int HKV>
+template <int HKV, int MAXC>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_chunks, const float* part) {
   constexpr int GH = 64 / HKV;
   const int h = blockIdx.x, t = blockIdx.y;
   const int g = h / GH, hc = h % GH;
   const int dv = threadIdx.x;
   const float* pp = part + ((size_t)(t * HKV + g) * n_chunks) * kPartFloats;
-  float mc[kMaxChunks], lc[kMaxChunks], oc[kMaxChunks];
+  float mc[MAXC], lc[MAXC], oc[MAXC];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < MAXC; ++c) {
     const bool ok = c < n_chunks;
-    const float* q = pp + (size_t)(ok ? c : 0) * kPartFloats;
-    mc[c] = ok ? q[hc] : -INFINITY;
-    lc[c] = ok ? q[16 + hc] : 0.f;
-    oc[c] = ok ? q[32 + hc * 128 + dv] : 0.f;
+    const float* q = pp + (size_t)(ok ? c : 0) * kPartFloats;   // chunk 0 stands in beyond n_chunks
+    const float m = q[hc], l = q[16 + hc], o = q[32 + hc * 128 + dv];
+    mc[c] = ok ? m : -INFINITY;
+    lc[c] = ok ? l : 0.f;
+    oc[c] = ok ? o : 0.f;
   }
   const float s2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
   float M = s2;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
+  for (int c = 0; c < MAXC; ++c) M = fmaxf(M, mc[c]);
   float L = 0.f, O = 0.f;
   if (M != -INFINITY) {
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
+    for (int c = 0; c < MAXC; ++c) {
       const float f = mc[c] == -INFINITY ? 0.f : exp2f(mc[c] - M);
       L += f * lc[c];
       O += f * oc[c];
@@ -125,14 +126,18 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* scratch, hipStream_t st) 
                      dim3(kSplitNW * 64), 0, st, a, n_used, chunk, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS>), dim3(64, a.T), dim3(128), 0, st, a, n_used,
-                     (const float*)part);
-  return hipGetLastError();
+  return launch_attn_merge(a, n_used, part, st);
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int n_chunks, const float* part, hipStream_t st) {
   if (n_chunks < 1 || n_chunks > kMaxChunks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS>), dim3(64, a.T), dim3(128), 0, st, a, n_chunks, part);
+  if (n_chunks <= 8)
+    hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS, 8>), dim3(64, a.T), dim3(128), 0, st, a, n_chunks, part);
+  else if (n_chunks <= 16)
+    hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS, 16>), dim3(64, a.T), dim3(128), 0, st, a, n_chunks, part);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<DSA_KV_HEADS, kMaxChunks>), dim3(64, a.T), dim3(128), 0, st, a,
+                       n_chunks, part);
   return hipGetLastError();
 }
 

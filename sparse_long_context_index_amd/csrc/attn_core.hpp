@@ -57,15 +57,17 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
   const int kg = lane >> 4;
   const float qscale = a.sm_scale * kLog2e;
 
-  // Q as the B operand: column = head, k-group kg covers dims 48*kg .. 48*kg+47
+  // Q as the B operand: column = head; k-step s, k-group kg covers dims
+  // 32 s + 8 kg .. + 7 (K uses the same order, so the 4 k-groups of a key row
+  // read 64 contiguous bytes per load)
   bf16x8 qf[6];
   {
     const bool hv = col < GH;
     const int h = g * GH + (hv ? col : 0);
-    const uint16_t* qp = a.q + ((size_t)t * 64 + h) * 192 + 48 * kg;
+    const uint16_t* qp = a.q + ((size_t)t * 64 + h) * 192 + 8 * kg;
 #pragma unroll
     for (int s = 0; s < 6; ++s) {
-      u16x8 raw = *reinterpret_cast<const u16x8*>(qp + 8 * s);
+      u16x8 raw = *reinterpret_cast<const u16x8*>(qp + 32 * s);
       if (!hv) raw = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
@@ -87,35 +89,41 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
     const int tb = p0 + tile * kTileKeys;
     bf16x8 pf;
     if (active) {
-      // ---- all index and row loads first: one dependent round trip per tile
-      const int kv = lane >> 1;                          // V staging: key lane/2, half lane&1
-      const int64_t rv = tb + kv < p1 ? src.row(tb + kv) : -1;
+      // ---- all index and row loads first: one dependent round trip per tile.
+      // Every load instruction reads whole runs of a few rows: K, 64 bytes of
+      // each of 16 rows; V, load i covers keys 4 i .. 4 i + 3, 16 lanes per
+      // 256-byte row.
       int64_t rk[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int p = tb + b * 16 + col;
         rk[b] = p < p1 ? src.row(p) : -1;
       }
+      int64_t rv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = tb + 4 * i + (lane >> 4);
+        rv[i] = p < p1 ? src.row(p) : -1;
+      }
       u16x8 kraw[2][6];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const uint16_t* kp = a.k + ((size_t)(rk[b] >= 0 ? rk[b] : 0) * HKV + g) * 192 + 48 * kg;
+        const uint16_t* kp = a.k + ((size_t)(rk[b] >= 0 ? rk[b] : 0) * HKV + g) * 192 + 8 * kg;
 #pragma unroll
-        for (int s = 0; s < 6; ++s) kraw[b][s] = *reinterpret_cast<const u16x8*>(kp + 8 * s);
+        for (int s = 0; s < 6; ++s) kraw[b][s] = *reinterpret_cast<const u16x8*>(kp + 32 * s);
       }
       u16x8 vraw[8];
-      {
-        const u16x8* sp = reinterpret_cast<const u16x8*>(a.v + ((size_t)(rv >= 0 ? rv : 0) * HKV + g) * 128 +
-                                                         (lane & 1) * 64);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vraw[i] = sp[i];
-      }
+      for (int i = 0; i < 8; ++i)
+        vraw[i] = *reinterpret_cast<const u16x8*>(a.v + ((size_t)(rv[i] >= 0 ? rv[i] : 0) * HKV + g) * 128 +
+                                                  8 * (lane & 15));
       // ---- stage V rows (an empty slot stages zeros, never the row it loaded)
       {
-        u16x8* dst = reinterpret_cast<u16x8*>(vs + kv * kVStride + (lane & 1) * 64);
         const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = rv >= 0 ? vraw[i] : zero;
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<u16x8*>(vs + (4 * i + (lane >> 4)) * kVStride + 8 * (lane & 15)) =
+              rv[i] >= 0 ? vraw[i] : zero;
       }
       // ---- QK for the two 16-key blocks
       f32x4 acc[2];

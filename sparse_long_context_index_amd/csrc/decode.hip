@@ -174,15 +174,25 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
         }
       __syncthreads();
     };
-    level(s1, 0xFFFu, 32, 0u, kHistBins);
+    // first digit: (key - L0) >> s1 over every entry >= L0
+    for (int i = tid; i < kHistBins; i += kDecNT) rs.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kLPT; ++q)
+#pragma unroll
+      for (int j = 0; j < kListM; ++j)
+        if ((uint32_t)j < n[q] && kA[q][j] >= L0) atomicAdd(&rs.hist[(kA[q][j] - L0) >> s1], 1u);
+    __syncthreads();
     find_threshold_bin<kDecNT, kHistBins>(rs.hist, (uint32_t)k, rs.scan, &rs.bin, &rs.above);
     const uint32_t b1 = rs.bin;
     uint32_t need = (uint32_t)k - rs.above;    // entries still to take from bin b1
     const uint32_t cnt1 = rs.hist[b1];
     __syncthreads();
+    const uint32_t lo = L0 + (b1 << s1);       // bin b1 holds the keys lo .. hi
+    const uint32_t wid = (1u << s1) - 1u;
+    const uint32_t hi = lo > 0xFFFFFFFFu - wid ? 0xFFFFFFFFu : lo + wid;
     auto in_b1 = [&](int q, int j) {
-      return (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] >= L0) &
-             (uint32_t)(((kA[q][j] - L0) >> s1) == b1);
+      return (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] >= lo) & (uint32_t)(kA[q][j] <= hi);
     };
     if (cnt1 <= (uint32_t)kC1Cap) {
       // rank the bin's entries directly; the one of rank need - 1 is the k-th
