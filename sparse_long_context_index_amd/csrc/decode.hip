@@ -49,6 +49,7 @@ struct DecodeShared {
       RadixShared rs;
       alignas(16) uint32_t ck[kC1Cap];             // entries of the threshold bin
       alignas(16) uint32_t ci[kC1Cap];
+      uint32_t rk[kC1Cap];                         // their ranks within the bin
       uint32_t tk, ti;                             // the k-th entry (key, index)
     } s;
     int32_t sorted[DSA_TOPK_MAX];
@@ -129,6 +130,8 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 
   // ---- 2. the k-th entry (tk, ti) of the union: keep key > tk, or key == tk and index <= ti
   bool fallback;
+  bool direct = false;                         // the kept set is already in sel
+  uint32_t n_sel_direct = 0;
   uint32_t tk = 0u, ti = 0xFFFFFFFFu;
   if (n_vis <= (int64_t)k) {
     fallback = any_full;                       // the lists hold every visible key only when uncapped
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     __syncthreads();
     find_threshold_bin<kDecNT, kHistBins>(rs.hist, (uint32_t)k, rs.scan, &rs.bin, &rs.above);
     const uint32_t b1 = rs.bin;
-    uint32_t need = (uint32_t)k - rs.above;    // entries still to take from bin b1
+    const uint32_t above1 = rs.above;          // entries in the bins above b1
+    uint32_t need = (uint32_t)k - above1;      // entries still to take from bin b1
     const uint32_t cnt1 = rs.hist[b1];
     __syncthreads();
     const uint32_t lo = L0 + (b1 << s1);       // bin b1 holds the keys lo .. hi
@@ -195,22 +199,34 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       return (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] >= lo) & (uint32_t)(kA[q][j] <= hi);
     };
     if (cnt1 <= (uint32_t)kC1Cap) {
-      // rank the bin's entries directly; the one of rank need - 1 is the k-th
-      uint32_t m = 0;
+      // Few entries in bin b1: the entries above the bin (a prefix of every
+      // list) are kept, and the bin's entries are ranked directly -- those of
+      // rank < need are kept too.  One packed prefix sum places both groups:
+      // [entries above the bin, in list order] then [kept bin entries by rank].
+      uint32_t ndq[kLPT], nd = 0, nb = 0;
 #pragma unroll
-      for (int q = 0; q < kLPT; ++q)
+      for (int q = 0; q < kLPT; ++q) {
+        ndq[q] = 0;
 #pragma unroll
-        for (int j = 0; j < kListM; ++j) m += in_b1(q, j);
+        for (int j = 0; j < kListM; ++j) {
+          ndq[q] += (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] > hi);
+          nb += in_b1(q, j);
+        }
+        nd += ndq[q];
+      }
       uint32_t tot;
-      uint32_t p = block_excl_scan<kDecNT>(m, sh.scan, &tot);
+      const uint32_t packed = block_excl_scan<kDecNT>((nd << 16) | nb, sh.scan, &tot);
+      uint32_t pb = packed & 0xFFFFu;
+      int last_slot = -1;                      // bin slot of this thread's capped list's last entry
 #pragma unroll
       for (int q = 0; q < kLPT; ++q)
 #pragma unroll
         for (int j = 0; j < kListM; ++j)
           if (in_b1(q, j)) {
-            sh.s.ck[p] = kA[q][j];
-            sh.s.ci[p] = iA[q][j];
-            ++p;
+            sh.s.ck[pb] = kA[q][j];
+            sh.s.ci[pb] = iA[q][j];
+            if (full[q] && (uint32_t)j + 1 == n[q]) last_slot = (int)pb;
+            ++pb;
           }
       const uint32_t ncp = (cnt1 + 15u) & ~15u;  // padded with key 0, which ranks below every entry
       if ((uint32_t)tid >= cnt1 && (uint32_t)tid < ncp) {
@@ -236,14 +252,29 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
             rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
                     before(k4[q].w, i4[q].w);
         }
-        if (rank == need - 1) {
-          sh.s.tk = key;
-          sh.s.ti = id;
-        }
+        sh.s.rk[tid] = rank;
       }
       __syncthreads();
-      tk = sh.s.tk;
-      ti = sh.s.ti;
+      // a capped list that keeps its last entry may hide winners
+      bool hides = false;
+#pragma unroll
+      for (int q = 0; q < kLPT; ++q) hides |= full[q] && n[q] == (uint32_t)kListM && kA[q][kListM - 1] > hi;
+      if (last_slot >= 0) hides |= sh.s.rk[last_slot] < need;
+      fallback = __syncthreads_or(hides);
+      if (!fallback) {
+        uint32_t pd = packed >> 16;
+#pragma unroll
+        for (int q = 0; q < kLPT; ++q) {
+#pragma unroll
+          for (int j = 0; j < kListM; ++j)      // the entries above the bin lead the list
+            if ((uint32_t)j < ndq[q] && pd + j < (uint32_t)DSA_TOPK_MAX) sh.sel[pd + j] = (int32_t)iA[q][j];
+          pd += ndq[q];
+        }
+        if ((uint32_t)tid < cnt1 && sh.s.rk[tid] < need && above1 + sh.s.rk[tid] < (uint32_t)DSA_TOPK_MAX)
+          sh.sel[above1 + sh.s.rk[tid]] = (int32_t)sh.s.ci[tid];
+        n_sel_direct = (uint32_t)k;
+        direct = true;
+      }
     } else {
       // a crowded bin: radix descent over its keys, then over the tied indices
       uint32_t known = b1, eq = cnt1;
@@ -270,53 +301,55 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
                                 rs, &tau2, &r2, &eq2);
         ti = ~tau2;
       }
+      fallback = false;
     }
-    fallback = false;
   }
 
   // ---- 3. the kept prefix of each list; a capped list keeping its last entry may hide winners
-  uint32_t cnt[kLPT];
+  uint32_t n_sel = n_sel_direct;
+  if (!direct) {
+    uint32_t cnt[kLPT];
 #pragma unroll
-  for (int q = 0; q < kLPT; ++q) cnt[q] = 0u;
-  if (!fallback) {
-    bool hides = false;
+    for (int q = 0; q < kLPT; ++q) cnt[q] = 0u;
+    if (!fallback) {
+      bool hides = false;
 #pragma unroll
-    for (int q = 0; q < kLPT; ++q) {
-      if (n_vis <= (int64_t)k) {
-        cnt[q] = n[q];
-      } else {
+      for (int q = 0; q < kLPT; ++q) {
+        if (n_vis <= (int64_t)k) {
+          cnt[q] = n[q];
+        } else {
+#pragma unroll
+          for (int j = 0; j < kListM; ++j)
+            cnt[q] += (uint32_t)((uint32_t)j < n[q]) &
+                      ((uint32_t)(kA[q][j] > tk) | ((uint32_t)(kA[q][j] == tk) & (uint32_t)(iA[q][j] <= ti)));
+        }
+        hides |= full[q] && cnt[q] == n[q];
+      }
+      fallback = __syncthreads_or(hides);
+    }
+    __syncthreads();
+
+    if (!fallback) {
+      uint32_t cnt_all = 0;
+#pragma unroll
+      for (int q = 0; q < kLPT; ++q) cnt_all += cnt[q];
+      uint32_t base = block_excl_scan<kDecNT>(cnt_all, sh.scan, &n_sel);
+#pragma unroll
+      for (int q = 0; q < kLPT; ++q) {
 #pragma unroll
         for (int j = 0; j < kListM; ++j)
-          cnt[q] += (uint32_t)((uint32_t)j < n[q]) &
-                    ((uint32_t)(kA[q][j] > tk) | ((uint32_t)(kA[q][j] == tk) & (uint32_t)(iA[q][j] <= ti)));
+          if ((uint32_t)j < cnt[q] && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[q][j];
+        base += cnt[q];
       }
-      hides |= full[q] && cnt[q] == n[q];
+      if (n_sel > (uint32_t)DSA_TOPK_MAX) n_sel = DSA_TOPK_MAX;
+    } else {
+      const float* row = d.scores + (int64_t)t * d.ld;
+      auto row_key = [&](int i) { return order_key(row[i]); };
+      uint32_t tau = 0, r = 0, eq = 0;
+      if (n_vis > (int64_t)k) radix_threshold<kDecNT>(row_key, (int)n_vis, (uint32_t)k, sh.s.rs, &tau, &r, &eq);
+      n_sel = ordered_keep<kDecNT>(row_key, (int)n_vis, tau, r, sh.scan,
+                                   [&](uint32_t pos, int i) { sh.sel[pos] = i; });
     }
-    fallback = __syncthreads_or(hides);
-  }
-  __syncthreads();
-
-  uint32_t n_sel;
-  if (!fallback) {
-    uint32_t cnt_all = 0;
-#pragma unroll
-    for (int q = 0; q < kLPT; ++q) cnt_all += cnt[q];
-    uint32_t base = block_excl_scan<kDecNT>(cnt_all, sh.scan, &n_sel);
-#pragma unroll
-    for (int q = 0; q < kLPT; ++q) {
-#pragma unroll
-      for (int j = 0; j < kListM; ++j)
-        if ((uint32_t)j < cnt[q] && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[q][j];
-      base += cnt[q];
-    }
-    if (n_sel > (uint32_t)DSA_TOPK_MAX) n_sel = DSA_TOPK_MAX;
-  } else {
-    const float* row = d.scores + (int64_t)t * d.ld;
-    auto row_key = [&](int i) { return order_key(row[i]); };
-    uint32_t tau = 0, r = 0, eq = 0;
-    if (n_vis > (int64_t)k) radix_threshold<kDecNT>(row_key, (int)n_vis, (uint32_t)k, sh.s.rs, &tau, &r, &eq);
-    n_sel = ordered_keep<kDecNT>(row_key, (int)n_vis, tau, r, sh.scan,
-                                 [&](uint32_t pos, int i) { sh.sel[pos] = i; });
   }
   __syncthreads();
 
