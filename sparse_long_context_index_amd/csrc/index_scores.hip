@@ -33,7 +33,8 @@ namespace dsa {
 namespace {
 
 constexpr int kScanUnroll = 4;   // 16-key tiles per wave in flight
-constexpr int kScanBlocks = 512; // persistent workgroups of the decode scan (2 per CU)
+constexpr int kScanBlocks = 512; // persistent workgroups of the list scan (2 per CU): one list each
+constexpr int kPlainScanBlocks = 768;   // persistent workgroups of the scan without lists (3 per CU)
 
 __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   // 32 bytes as two 16-byte loads (only 16-byte alignment is guaranteed)
@@ -81,15 +82,16 @@ __device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
   }
 }
 
-// Decode scan.  16-key tiles are dealt round-robin to the workgroups (tile j
-// belongs to workgroup j % G), so at any moment the chip streams one
-// contiguous stretch of the key cache and any run of consecutive keys is
-// spread over many workgroups.  Each wave takes kScanUnroll of its
-// workgroup's tiles per step, loads each with fully coalesced 16-byte loads
-// (1 KiB per instruction), stages it in a wave-private LDS area with a padded
-// row stride, and reads it back in MFMA operand order (key = lane % 16, 32
-// bytes of k-group lane / 16).  The next step's loads are in flight while the
-// current one is scored.
+// Decode scan.  Without lists, persistent workgroups (3 per CU) take groups
+// of 16 consecutive 16-key tiles in grid-stride order.  With lists, 16-key
+// tiles are dealt round-robin to the workgroups (tile j belongs to workgroup
+// j % G), so any run of consecutive keys is spread over many workgroups and
+// their lists.  Either way the chip streams one contiguous stretch of the key
+// cache at any moment.  Each wave takes kScanUnroll tiles per step, loads each
+// with fully coalesced 16-byte loads (1 KiB per instruction), stages it in a
+// wave-private LDS area with a padded row stride, and reads it back in MFMA
+// operand order (key = lane % 16, 32 bytes of k-group lane / 16).  The next
+// step's loads are in flight while the current one is scored.
 //
 // with_hist: also build the level-1 radix histogram of the scores (top-k's
 // first digit) with two 16-bit counters per LDS word; the workgroup adds its
@@ -261,11 +263,13 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   const int64_t G = gridDim.x;
   uint8_t* st = stage + wave * kScanUnroll * 16 * kStageRow;
   i32x4 buf[2 * kScanUnroll];
-  // local tile lt of this workgroup is global tile blockIdx.x + G * lt; step
-  // `it` gives wave w the local tiles 16 it + kScanUnroll w + u; load i covers
-  // 8 keys of tile i / 2
+  // With lists, local tile lt of this workgroup is global tile blockIdx.x +
+  // G * lt and step `it` gives wave w the local tiles 16 it + kScanUnroll w +
+  // u; without, step `it` covers the group of 16 consecutive tiles blockIdx.x
+  // + G * it, kScanUnroll of them per wave.  Load i covers 8 keys of tile i / 2.
   auto tile_of = [&](int it, int u) -> int64_t {
-    return (int64_t)blockIdx.x + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
+    if (kLists) return (int64_t)blockIdx.x + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
+    return ((int64_t)blockIdx.x + G * (int64_t)it) * 4 * kScanUnroll + wave * kScanUnroll + u;
   };
   auto load_step = [&](int it) {
 #pragma unroll
@@ -276,9 +280,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     }
   };
 
-  (void)ngroups;
-  const int64_t n_local = cdiv(ntiles - blockIdx.x, G);         // tiles of this workgroup
-  const int n_steps = (int)cdiv(n_local, 4 * kScanUnroll);
+  const int n_steps = kLists ? (int)cdiv(cdiv(ntiles - blockIdx.x, G), 4 * kScanUnroll)
+                             : (int)cdiv(ngroups - blockIdx.x, G);
   int iter = 0;
   if (n_steps > 0) load_step(0);
   for (; iter < n_steps; ++iter) {
@@ -476,9 +479,16 @@ int scan_grid(int64_t Lk) {
   return (int)(ngroups < kScanBlocks ? ngroups : kScanBlocks);
 }
 
+// the scan without lists streams groups of 16 consecutive tiles with 3
+// workgroups per CU
+static int plain_scan_grid(int64_t Lk) {
+  const int64_t ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
+  return (int)(ngroups < kPlainScanBlocks ? ngroups : kPlainScanBlocks);
+}
+
 int scan_list_cap(int64_t Lk) {
-  const int64_t local_tiles = cdiv(cdiv(Lk, 16), scan_grid(Lk));   // workgroup 0 has the most
-  return (int)(cdiv(local_tiles, 4 * kScanUnroll) * 4 * kScanUnroll * 16);
+  const int64_t ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
+  return (int)(cdiv(ngroups, plain_scan_grid(Lk)) * 4 * kScanUnroll * 16);   // workgroup 0 has the most
 }
 
 size_t scan_lds_bytes(int64_t Lk, int T, bool lists) {
@@ -498,7 +508,7 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
     const int64_t ntiles = cdiv(Lk, 16);
     const int64_t ngroups = cdiv(ntiles, 4 * kScanUnroll);
     // 16-bit histogram counters: a workgroup must see fewer than 65536 keys
-    const int64_t grid = scan_grid(Lk);
+    const int64_t grid = lists.keys ? scan_grid(Lk) : plain_scan_grid(Lk);
     if (with_hist && scan_list_cap(Lk) >= 65536) return hipErrorInvalidValue;
     const size_t lds = scan_lds_bytes(Lk, T, lists.keys != nullptr) +
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);

@@ -23,7 +23,7 @@ struct ScanLists {
   uint32_t* count = nullptr;   // [T][scan_grid] kept | (more than kListM visible) << 31
 };
 int scan_grid(int64_t Lk);     // workgroups of the decode scan
-int scan_list_cap(int64_t Lk); // keys a scan workgroup scores per row (at most)
+int scan_list_cap(int64_t Lk); // keys a workgroup of the scan without lists scores per row (at most)
 size_t scan_lds_bytes(int64_t Lk, int T, bool lists);   // dynamic LDS of the decode scan
 // topk_counters: optional workspace counter region; when given (T <=
 // kScanHistTMax) the scan also builds the top-k's level-1 histogram there.
