@@ -51,7 +51,9 @@ PLANT_GAMMA = 8.0
 # tensor -> spawn-child slot; fixed so that adding a tensor never reshuffles
 # the streams of the others.
 _SLOTS = {"q_idx": 0, "w": 1, "k_idx": 2, "q": 3, "k": 4, "v": 5, "sink": 6,
-          "plant_pos": 7, "plant_tok": 8, "seq_len": 9}
+          "plant_pos": 7, "plant_tok": 8, "seq_len": 9,
+          "ap_idx_q": 10, "ap_idx_k": 11, "ap_q": 12, "ap_k": 13, "ap_v": 14,
+          "ln_gamma": 15, "ln_beta": 16}
 
 _CHUNK = 1 << 22  # elements per generation/encoding chunk
 
@@ -228,3 +230,21 @@ def sample_rows(T: int, n: int = 64, seed: int = 4) -> np.ndarray:
 
 BF16_NAN = np.uint16(0x7FC0)
 E4M3_NAN = np.uint8(0x7F)
+
+
+def append_inputs(T: int, seed: int, n_kv_heads: int = DSA_KV_HEADS) -> Dict[str, np.ndarray]:
+    """Post-projection activations of T new tokens for the cache-append step.
+
+    idx_q [T,16,128], idx_k [T,128], q [T,64,192], k [T,Hkv,192], v [T,Hkv,128]
+    as bf16 bit patterns of N(0,1) draws; ln_gamma = 1 + 0.1 N(0,1) and
+    ln_beta = 0.1 N(0,1) float32 [128] stand in for the index key's LayerNorm
+    gain and bias."""
+    return {
+        "idx_q": encode_bf16(normal_f32(_rng(seed, "ap_idx_q"), (T, IDX_HEADS, IDX_DIM))),
+        "idx_k": encode_bf16(normal_f32(_rng(seed, "ap_idx_k"), (T, IDX_DIM))),
+        "q": encode_bf16(normal_f32(_rng(seed, "ap_q"), (T, Q_HEADS, QK_DIM))),
+        "k": encode_bf16(normal_f32(_rng(seed, "ap_k"), (T, n_kv_heads, QK_DIM))),
+        "v": encode_bf16(normal_f32(_rng(seed, "ap_v"), (T, n_kv_heads, V_DIM))),
+        "ln_gamma": (1.0 + 0.1 * normal_f32(_rng(seed, "ln_gamma"), (IDX_DIM,))).astype(np.float32),
+        "ln_beta": (0.1 * normal_f32(_rng(seed, "ln_beta"), (IDX_DIM,))).astype(np.float32),
+    }

@@ -1,0 +1,159 @@
+"""Pins for the cache-append oracle (oracle/cache_append.py): every function is
+checked against something other than itself -- library casts on values where
+a single rounding is unambiguous, closed forms of LayerNorm, and the algebraic
+properties that define a rotary position encoding (identity at position 0,
+pair norms kept, inner products depending only on the position difference,
+the complex-number form), plus brute force on a tiny case.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cache_append as ca
+from oracle import dsa_oracle as do
+
+
+# ---------------------------------------------------------------- roundings
+
+def test_e4m3_rounding_matches_torch_on_float32_values():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-12, 7, 100000))).astype(np.float32)
+    ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ca.to_e4m3(x.astype(np.float64)), ref)
+
+
+def test_e4m3_codes_round_trip_and_ties_go_to_even():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = do.decode_e4m3(codes)
+    out = ca.to_e4m3(vals)
+    # -0.0 and +0.0 keep their sign bit; every other code maps to itself
+    assert np.array_equal(out, codes)
+    # midpoints between neighbouring positive codes round to the even code
+    pos = np.arange(0, 0x7E, dtype=np.uint8)
+    lo, hi = do.decode_e4m3(pos), do.decode_e4m3(pos + 1)
+    mid = (lo + hi) / 2
+    got = ca.to_e4m3(mid)
+    want = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    assert np.array_equal(got, want)
+    # saturation instead of NaN
+    assert ca.to_e4m3(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]
+
+
+def test_bf16_rounding_matches_torch_and_ties_go_to_even():
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-30, 30, 100000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ca.to_bf16(x.astype(np.float64)), ref)
+    # 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7: ties to even (1.0)
+    assert ca.to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 0x3F80
+    assert ca.to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 0x3F82
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def test_layer_norm_closed_forms():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((5, 128)) * 3 + 7
+    y = ca.layer_norm(x, None, None, eps=0.0)
+    assert np.allclose(y.mean(axis=-1), 0, atol=1e-12)
+    assert np.allclose((y ** 2).mean(axis=-1), 1, atol=1e-12)
+    # eps shrinks the variance to var / (var + eps)
+    var = x.var(axis=-1)
+    y2 = ca.layer_norm(x, None, None, eps=0.5)
+    assert np.allclose((y2 ** 2).mean(axis=-1), var / (var + 0.5), rtol=1e-12)
+    # gain and bias act per dim after the normalisation
+    g, b = rng.standard_normal(128), rng.standard_normal(128)
+    assert np.allclose(ca.layer_norm(x, g, b, eps=0.0), y * g + b, atol=1e-12)
+    # a constant row normalises to zero (then the bias)
+    c = np.full((1, 128), 2.5)
+    assert np.allclose(ca.layer_norm(c, g, b), b)
+    # shift and positive scale invariance
+    assert np.allclose(ca.layer_norm(4 * x - 9, None, None, eps=0.0), y, atol=1e-12)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rotary_dims_are_a_third_of_each_head():
+    # [NoFA] "Inside a DSA layer": partial_rotary_factor 0.334 on every head
+    assert ca.rotary_dims(128) == 42
+    assert ca.rotary_dims(192) == 64
+
+
+def test_rope_identity_at_zero_and_passthrough_dims():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((3, 4, 192))
+    assert np.array_equal(ca.rope(x, [0, 0, 0], 64, 1e7), x)
+    y = ca.rope(x, [5, 1000, 999999], 64, 1e7)
+    assert np.array_equal(y[..., 64:], x[..., 64:])
+
+
+def test_rope_keeps_pair_norms_and_matches_the_complex_form():
+    rng = np.random.default_rng(15)
+    R, base = 42, 1e7
+    x = rng.standard_normal((4, 128))
+    pos = [3, 77, 4096, 1048576]
+    y = ca.rope(x, pos, R, base)
+    h = R // 2
+    assert np.allclose(x[:, :h] ** 2 + x[:, h:R] ** 2, y[:, :h] ** 2 + y[:, h:R] ** 2, rtol=1e-12)
+    # the pair (i, i + h) is the complex number x_i + j x_{i+h} times e^{j a_i}
+    i = np.arange(h)
+    for row, p in enumerate(pos):
+        z = (x[row, :h] + 1j * x[row, h:R]) * np.exp(1j * p * base ** (-2.0 * i / R))
+        assert np.allclose(y[row, :h], z.real, atol=1e-12)
+        assert np.allclose(y[row, h:R], z.imag, atol=1e-12)
+
+
+def test_rope_inner_products_depend_only_on_the_position_difference():
+    rng = np.random.default_rng(16)
+    R, base = 64, 1e4
+    q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    m, n = 1234, 1001
+    lhs = float(ca.rope(q, [m], R, base) @ ca.rope(k, [n], R, base).T)
+    rhs = float(ca.rope(q, [m - n], R, base) @ k.T)
+    assert math.isclose(lhs, rhs, rel_tol=1e-10, abs_tol=1e-10)
+
+
+def test_rope_brute_force_tiny():
+    x = np.array([[1.0, 2.0, 3.0, 4.0, 5.0, 6.0]])
+    R, base, p = 4, 100.0, 3
+    want = x.copy()
+    for i in range(R // 2):
+        a = p * base ** (-2.0 * i / R)
+        u, v = x[0, i], x[0, i + R // 2]
+        want[0, i] = u * math.cos(a) - v * math.sin(a)
+        want[0, i + R // 2] = v * math.cos(a) + u * math.sin(a)
+    assert np.allclose(ca.rope(x, [p], R, base), want, atol=1e-14)
+
+
+def test_rope_mutant_with_a_flipped_sign_fails_the_relative_pin():
+    rng = np.random.default_rng(17)
+    R, base = 64, 1e4
+
+    def bad_rope(x, pos, R, base):
+        y = ca.rope(x, pos, R, base)
+        h = R // 2
+        ang = ca.rope_angles(pos, R, base)
+        y[..., :h] = x[..., :h] * np.cos(ang) + x[..., h:R] * np.sin(ang)
+        return y
+
+    q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    m, n = 1234, 1001
+    lhs = float(bad_rope(q, [m], R, base) @ bad_rope(k, [n], R, base).T)
+    rhs = float(bad_rope(q, [m - n], R, base) @ k.T)
+    assert not math.isclose(lhs, rhs, rel_tol=1e-6)
+
+
+# ---------------------------------------------------------------- the whole step
+
+def test_cache_append_composes_the_steps():
+    from sparse_long_context_index_amd import synth
+    inp = synth.append_inputs(T=2, seed=5)
+    out = ca.cache_append(inp, Lk=1000, T=2)
+    pos = np.array([998, 999])
+    ik = ca.rope(ca.layer_norm(do.decode_bf16(inp["idx_k"]), inp["ln_gamma"], inp["ln_beta"]), pos, 42, 1e7)
+    assert np.array_equal(out["idx_k"], ca.to_e4m3(ik))
+    assert np.array_equal(out["v"], inp["v"])
+    # pass-through dims of q are the inputs exactly (bf16 in, bf16 out)
+    assert np.array_equal(out["q"][..., 64:], inp["q"][..., 64:])
