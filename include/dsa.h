@@ -201,6 +201,53 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
                            float* scores_out, int64_t ld_scores,
                            void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * dsa_cache_append -- the step before the index sweep for T new tokens at
+ * positions p_t = Lk - T + t ([NoFA] "Inside a DSA layer" and Figure 1, panel
+ * B: the index key is layer-normalised, rotated by partial RoPE and rounded to
+ * fp8; the index queries are rotated and rounded to fp8; the attention
+ * queries and keys are rotated (RoPE on a third of each head, rope base
+ * 10,000,000 on the sparse layers, same section); keys and values are
+ * appended to the cache):
+ *
+ *   idx_k' = rope(LayerNorm(idx_k) * ln_gamma + ln_beta, p)  -> fp8 -> k_idx_cache[p]
+ *   idx_q' = rope(idx_q, p)                                   -> fp8 -> q_idx_out
+ *   q'     = rope(q, p)                                       -> bf16 -> q_out
+ *   k'     = rope(k, p)                                       -> bf16 -> k_cache[p]
+ *   v                                                         -> v_cache[p]
+ *
+ * rope(x, p) rotates the first R dims of every head, pairing dim i with dim
+ * i + R/2: x_i cos a_i - x_{i+R/2} sin a_i and x_{i+R/2} cos a_i + x_i sin a_i,
+ * a_i = p * rope_base^(-2i/R); the angles are formed in float64 at the
+ * absolute position ("How much of this did AI actually build?" reports
+ * precision issues in positional encoding).  Dims >= R pass through.
+ *
+ *   idx_q        [T][16][128] bf16   index query heads (post-projection)
+ *   idx_k        [T][128] bf16       index key
+ *   ln_gamma, ln_beta [128] float32  LayerNorm gain and bias (NULL: 1 and 0)
+ *   ln_eps       LayerNorm epsilon (>= 0)
+ *   q            [T][64][192] bf16   attention queries
+ *   k, v         [T][4][192], [T][4][128] bf16  attention keys and values
+ *   rot_idx, rot_main  rotated dims of the 128- and 192-dim heads (even,
+ *                      0 < R <= head dim; the pages' third: 42 and 64)
+ *   rope_base    > 0 (DSA_ROPE_BASE for the sparse layers)
+ *   q_idx_out    [T][16][128] fp8    the scan's query (dsa_index_scores q_idx)
+ *   k_idx_cache  [Lk][128] fp8       rows Lk-T .. Lk-1 written
+ *   q_out        [T][64][192] bf16
+ *   k_cache      [Lk][4][192] bf16   rows Lk-T .. Lk-1 written
+ *   v_cache      [Lk][4][128] bf16   rows Lk-T .. Lk-1 written
+ *
+ * fp8 results round to nearest even after clamping to +-448; bf16 results
+ * round to nearest even.  Arithmetic is float32 (LayerNorm moments float64).
+ * Limits: 1 <= T <= Lk < 2^31, T <= 8192.  Needs no workspace.
+ */
+#define DSA_ROPE_BASE 10000000.0
+dsa_status dsa_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
+                            const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, int64_t Lk, int32_t T, int32_t rot_idx, int32_t rot_main,
+                            double rope_base, uint8_t* q_idx_out, uint8_t* k_idx_cache, uint16_t* q_out,
+                            uint16_t* k_cache, uint16_t* v_cache, void* stream);
+
 /* Workspace bytes needed by `op` for the given sizes (B is the SWA batch; the
  * other sizes are ignored where they do not apply).  Returns 0 for an invalid
  * request.  Sizes are upper bounds: a workspace sized for (Lk, T, k, B) serves

@@ -6,7 +6,7 @@ kernels.  There is no fallback: if the library is missing, or a tensor is not
 on a GPU, the call raises.
 
 Functions carry the C names: dsa_index_scores, dsa_topk, sparse_gqa_attn,
-swa_attn, dsa_decode_step, plus the workspace helpers.  Tensors are torch
+swa_attn, dsa_decode_step, dsa_cache_append, plus the workspace helpers.  Tensors are torch
 tensors on the GPU with the layouts of dsa.h (uint8 for fp8 bytes, bfloat16
 or int16/uint16 for bf16, float32, int32, int64).
 """
@@ -26,6 +26,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPP
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP = range(5)
 
 IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
+ROPE_BASE = 1.0e7          # DSA_ROPE_BASE
+ROT_IDX, ROT_MAIN = 42, 64  # a third of the 128- and 192-dim heads
 DSA_KV_HEADS, SWA_KV_HEADS, TOPK_MAX, DECODE_T_MAX = 4, 8, 2048, 8
 
 _P = ctypes.c_void_p
@@ -41,6 +43,8 @@ _SIGS = {
     "swa_attn": ([_P, _P, _P, _I64, _P, _P, _I32, _I32, _P, _F, _P, _P, _P, _SZ, _P], _I32),
     "dsa_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _P, _F, _P, _P, _P, _P, _I64,
                          _P, _SZ, _P], _I32),
+    "dsa_cache_append": ([_P, _P, _P, _P, _F, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
+                          _P, _P, _P, _P, _P, _P], _I32),
     "dsa_workspace_bytes": ([_I32, _I64, _I32, _I32, _I32], _SZ),
     "dsa_workspace_init": ([_P, _SZ, _P], _I32),
     "dsa_status_string": ([_I32], ctypes.c_char_p),
@@ -180,3 +184,21 @@ def dsa_decode_step(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: in
                                   _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld,
                                   ws.ptr, ws.nbytes, _stream()), "dsa_decode_step")
     return out
+
+
+def dsa_cache_append(idx_q, idx_k, q, k, v, Lk: int, T: int, k_idx_cache, k_cache, v_cache,
+                     ln_gamma=None, ln_beta=None, ln_eps: float = 1e-6, rot_idx: int = ROT_IDX,
+                     rot_main: int = ROT_MAIN, rope_base: float = ROPE_BASE, q_idx_out=None, q_out=None):
+    """Append T new tokens (positions Lk-T .. Lk-1) to the index-key and K/V
+    caches; returns (q_idx_out [T,16,128] uint8, q_out [T,64,192] bf16)."""
+    dev = idx_q.device
+    if q_idx_out is None:
+        q_idx_out = torch.empty((T, IDX_HEADS, IDX_DIM), dtype=torch.uint8, device=dev)
+    if q_out is None:
+        q_out = torch.empty((T, Q_HEADS, QK_DIM), dtype=torch.bfloat16, device=dev)
+    _check(load().dsa_cache_append(_dev(idx_q, "idx_q"), _dev(idx_k, "idx_k"), _dev(ln_gamma, "ln_gamma"),
+                                   _dev(ln_beta, "ln_beta"), ln_eps, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                   Lk, T, rot_idx, rot_main, rope_base, _dev(q_idx_out, "q_idx_out"),
+                                   _dev(k_idx_cache, "k_idx_cache"), _dev(q_out, "q_out"), _dev(k_cache, "k_cache"),
+                                   _dev(v_cache, "v_cache"), _stream()), "dsa_cache_append")
+    return q_idx_out, q_out

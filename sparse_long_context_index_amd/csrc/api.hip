@@ -254,4 +254,26 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
   return hip_status(launch_sparse_attn(a, base + L.attn, st));
 }
 
+dsa_status dsa_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
+                            const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, int64_t Lk, int32_t T, int32_t rot_idx, int32_t rot_main,
+                            double rope_base, uint8_t* q_idx_out, uint8_t* k_idx_cache, uint16_t* q_out,
+                            uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+  const void* req[] = {idx_q, idx_k, q, k, v, q_idx_out, k_idx_cache, q_out, k_cache, v_cache};
+  for (const void* ptr : req) {
+    if (!ptr) return DSA_ERR_NULL;
+    if (!aligned16(ptr)) return DSA_ERR_ALIGN;
+  }
+  if ((ln_gamma && !aligned16(ln_gamma)) || (ln_beta && !aligned16(ln_beta))) return DSA_ERR_ALIGN;
+  if (T < 1 || T > 8192 || Lk < T || Lk >= kMaxLk) return DSA_ERR_SHAPE;
+  if (rot_idx < 2 || rot_idx > DSA_IDX_DIM || (rot_idx & 1) || rot_main < 2 || rot_main > DSA_QK_DIM ||
+      (rot_main & 1))
+    return DSA_ERR_SHAPE;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base) || !(ln_eps >= 0.f) || !std::isfinite(ln_eps))
+    return DSA_ERR_SHAPE;
+  return hip_status(launch_cache_append(idx_q, idx_k, ln_gamma, ln_beta, ln_eps, q, k, v, Lk, T, rot_idx,
+                                        rot_main, rope_base, q_idx_out, k_idx_cache, q_out, k_cache, v_cache,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"

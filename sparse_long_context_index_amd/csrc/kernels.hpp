@@ -83,6 +83,13 @@ struct DecodeArgs {
 int decode_chunks(int k);
 hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 
+// ---- cache append (LayerNorm / partial RoPE / fp8 of the indexer, RoPE of attention q, k)
+hipError_t launch_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
+                               const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, int64_t Lk, int T, int rot_idx, int rot_main, double base,
+                               uint8_t* q_idx_out, uint8_t* k_idx_cache, uint16_t* q_out, uint16_t* k_cache,
+                               uint16_t* v_cache, hipStream_t st);
+
 // ---- workspace
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -128,3 +128,24 @@ def test_binding_refuses_cpu_tensors(L):
     x = torch.zeros(16, dtype=torch.uint8)
     with pytest.raises(binding.DsaError):
         binding.dsa_index_scores(x, x, x, 1, 1, scores=torch.zeros(1, 1))
+
+
+def test_cache_append_validation(L):
+    f = L.dsa_cache_append
+    ok = [A] * 4
+    def call(idx_q=A, idx_k=A, g=None, b=None, eps=1e-6, q=A, k=A, v=A, Lk=100, T=1, ri=42, rm=64,
+             base=1e7, qo=A, kc=A, qq=A, kk=A, vv=A):
+        return f(idx_q, idx_k, g, b, eps, q, k, v, Lk, T, ri, rm, base, qo, kc, qq, kk, vv, None)
+    assert call(idx_q=None) == 1
+    assert call(vv=None) == 1
+    assert call(k=MIS) == 4
+    assert call(g=MIS) == 4
+    assert call(T=0) == 2
+    assert call(Lk=0) == 2
+    assert call(T=8193, Lk=10000) == 2
+    assert call(ri=43) == 2                 # odd rotary dims
+    assert call(rm=194) == 2                # beyond the head
+    assert call(ri=0) == 2
+    assert call(base=0.0) == 2
+    assert call(base=float("nan")) == 2
+    assert call(eps=-1.0) == 2

@@ -1,0 +1,195 @@
+"""GPU parity of the cache-append step (dsa_cache_append) against the fp64
+oracle (oracle/cache_append.py), through the C ABI.
+
+Bar.  The kernel forms each rotated value in fp32 from exact bf16 inputs and
+fp32 cos/sin of fp64 angles: |y - y_exact| <= 2^-24 (2|a c| + 2|b s| + |y|)
+< 2^-22 (|a| + |b|) for the pair (a, b) a rotated dim reads.  The index key's
+LayerNorm is formed in fp64 and rounded once to fp32 before the gain and bias,
+adding at most 2^-23 (|n g| + |beta|) per input.  The test allows twice that:
+B = 2^-21 * (sum of the magnitudes an output reads), and requires the GPU's
+code to be the rounding of some value within B of the exact value (rounding
+is monotone, so it lies between round(y - B) and round(y + B)).  B is far
+below one fp8 or bf16 step, so away from rounding midpoints the codes must be
+equal; values that pass through unrotated and unnormalised (B = 0) must be
+bit-identical.  Cache rows outside the appended positions are poisoned with a
+sentinel and must be left as they were.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cache_append as ca
+from sparse_long_context_index_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+SENT8 = 0x5A
+SENT16 = 0x7E5A
+REL = 2.0 ** -21
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    return torch.device("cuda", 0)
+
+
+def g(a, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev)
+
+
+def pair_mag(m, R):
+    """For each output dim: the magnitudes it reads -- m_i + m_{i+R/2} on a
+    rotated pair, m_d beyond R (m holds per-input magnitudes on the last axis)."""
+    h = R // 2
+    out = m.copy()
+    out[..., :h] = m[..., :h] + m[..., h:R]
+    out[..., h:R] = m[..., :h] + m[..., h:R]
+    return out
+
+
+def check_rounded(got, exact, B, kind, what):
+    rnd, dec = (ca.to_e4m3, oracle.decode_e4m3) if kind == "e4m3" else (ca.to_bf16, oracle.decode_bf16)
+    got = np.asarray(got)
+    lo = dec(rnd(exact - B)).astype(np.float64)
+    hi = dec(rnd(exact + B)).astype(np.float64)
+    v = dec(got).astype(np.float64)
+    ok = (v >= lo) & (v <= hi)
+    assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} codes outside the bound"
+    exact_codes = rnd(exact)
+    z = B == 0
+    assert np.array_equal(got[z], exact_codes[z]), f"{what}: pass-through values changed"
+    return int((got != exact_codes).sum())
+
+
+def run_append(dev, inp, Lk, T, ln=True, idx_fill=SENT8, kv_fill=SENT16):
+    kic = torch.full((Lk, 128), idx_fill, dtype=torch.uint8, device=dev)
+    kc = torch.full((Lk, 4, 192), kv_fill, dtype=torch.int16, device=dev)
+    vc = torch.full((Lk, 4, 128), kv_fill, dtype=torch.int16, device=dev)
+    qi, qo = binding.dsa_cache_append(
+        g(inp["idx_q"], dev), g(inp["idx_k"], dev), g(inp["q"], dev), g(inp["k"], dev), g(inp["v"], dev),
+        Lk, T, kic, kc.view(torch.bfloat16), vc.view(torch.bfloat16),
+        ln_gamma=g(inp["ln_gamma"], dev) if ln else None, ln_beta=g(inp["ln_beta"], dev) if ln else None)
+    torch.cuda.synchronize()
+    p0 = Lk - T
+    # nothing outside rows p0 .. Lk-1 was written
+    assert not bool((kic[:p0] != idx_fill).any()), "index-key cache written outside the new rows"
+    assert not bool((kc[:p0] != kv_fill).any()), "K cache written outside the new rows"
+    assert not bool((vc[:p0] != kv_fill).any()), "V cache written outside the new rows"
+    return {
+        "idx_q": qi.cpu().numpy(), "q": qo.view(torch.int16).cpu().numpy().view(np.uint16),
+        "idx_k": kic[p0:].cpu().numpy(), "k": kc[p0:].cpu().numpy().view(np.uint16),
+        "v": vc[p0:].cpu().numpy().view(np.uint16),
+    }
+
+
+def check_append(out, inp, Lk, T, ln=True):
+    ref_inp = dict(inp)
+    if not ln:
+        ref_inp["ln_gamma"] = None
+        ref_inp["ln_beta"] = None
+    ref = ca.cache_append(ref_inp, Lk, T)
+    ri, rm = ca.rotary_dims(128), ca.rotary_dims(192)
+    # the index key: magnitudes |n g| + |beta| of the normalised key
+    n = ca.layer_norm(oracle.decode_bf16(inp["idx_k"]), None, None)
+    gam = inp["ln_gamma"].astype(np.float64) if ln else np.ones(128)
+    bet = inp["ln_beta"].astype(np.float64) if ln else np.zeros(128)
+    Bk = REL * pair_mag(np.abs(n * gam) + np.abs(bet), ri)
+    diff = check_rounded(out["idx_k"], ref["idx_k_exact"], Bk, "e4m3", "index key")
+    for name, R, kind in (("idx_q", ri, "e4m3"), ("q", rm, "bf16"), ("k", rm, "bf16")):
+        x = np.abs(oracle.decode_bf16(inp[name]).astype(np.float64))
+        B = REL * pair_mag(x, R)
+        B[..., R:] = 0.0                               # unrotated bf16 inputs pass through exactly
+        diff += check_rounded(out[name], ref[name + "_exact"], B, kind, name)
+    assert np.array_equal(out["v"], ref["v"])
+    return diff
+
+
+@pytest.mark.parametrize("T,Lk", [(1, 1), (1, 8192), (4, 131072), (3, 1000), (8, 1048576), (1, 1048576),
+                                  (64, 70000)])
+def test_cache_append(dev, T, Lk):
+    inp = synth.append_inputs(T, seed=T * 7 + Lk % 1000)
+    out = run_append(dev, inp, Lk, T)
+    check_append(out, inp, Lk, T)
+
+
+def test_cache_append_without_layer_norm_gain_and_bias(dev):
+    inp = synth.append_inputs(5, seed=77)
+    out = run_append(dev, inp, 4096, 5, ln=False)
+    check_append(out, inp, 4096, 5, ln=False)
+
+
+def test_cache_append_extreme_values(dev):
+    # large activations saturate the fp8 codes at +-448; tiny ones land in the
+    # e4m3 subnormal range; a constant index key normalises to the bias alone
+    T, Lk = 4, 5000
+    inp = synth.append_inputs(T, seed=9)
+    rng = np.random.default_rng(9)
+    big = (rng.standard_normal((T, 16, 128)) * np.array([1e3, 1e-3, 1.0, 3e2])[:, None, None]).astype(np.float32)
+    inp["idx_q"] = synth.encode_bf16(big)
+    inp["idx_k"] = inp["idx_k"].copy()
+    inp["idx_k"][1] = inp["idx_k"][1, 0]
+    inp["q"] = synth.encode_bf16((rng.standard_normal((T, 64, 192)) * 1e30).astype(np.float32))
+    out = run_append(dev, inp, Lk, T)
+    check_append(out, inp, Lk, T)
+    assert np.any((out["idx_q"] & 0x7F) == 0x7E), "no saturated fp8 code was exercised"
+
+
+def test_cache_append_prefill_chunk_sampled(dev):
+    # the full prefill chunk: 8192 new tokens onto a 1,048,576-token history;
+    # the oracle checks a seeded sample of tokens, each at its own position
+    T, L = 8192, 1048576
+    Lk = L + T
+    inp = synth.append_inputs(T, seed=21)
+    out = run_append(dev, inp, Lk, T)
+    for t in synth.sample_rows(T, 64, seed=21):
+        t = int(t)
+        one = {k_: v_[t:t + 1] if v_.ndim > 1 else v_ for k_, v_ in inp.items()}
+        got = {k_: v_[t:t + 1] for k_, v_ in out.items()}
+        check_append(got, one, Lk - T + t + 1, 1)
+
+
+def test_cache_append_then_decode_step(dev):
+    # the appended rows feed the decode step exactly as the oracle's do
+    cfg = synth.DecodeConfig("a", L=6000, T=2, k=512, plant_frac=0.01, seed=12)
+    d = synth.decode_inputs(cfg)
+    Lk, T = cfg.Lk, cfg.T
+    inp = synth.append_inputs(T, seed=12)
+    kic = g(d["k_idx"], dev)
+    kc, vc = g(d["k"], dev), g(d["v"], dev)
+    qi, qo = binding.dsa_cache_append(
+        g(inp["idx_q"], dev), g(inp["idx_k"], dev), g(inp["q"], dev), g(inp["k"], dev), g(inp["v"], dev),
+        Lk, T, kic, kc.view(torch.bfloat16), vc.view(torch.bfloat16),
+        ln_gamma=g(inp["ln_gamma"], dev), ln_beta=g(inp["ln_beta"], dev))
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+    scores = torch.empty((T, Lk), dtype=torch.float32, device=dev)
+    out = binding.dsa_decode_step(qi, g(d["w"], dev), kic, qo, kc.view(torch.bfloat16), vc.view(torch.bfloat16),
+                                  Lk, T, cfg.k, g(d["sink"], dev), float(d["sm_scale"]), idx_out=idx,
+                                  scores_out=scores)
+    torch.cuda.synchronize()
+    # the oracle's inputs: the caches with the GPU-appended rows (checked
+    # against the oracle's own append here) and the GPU-rotated queries
+    d2 = dict(d)
+    d2["k_idx"] = kic.cpu().numpy()
+    d2["k"] = kc.cpu().numpy().view(np.uint16)
+    d2["v"] = vc.cpu().numpy().view(np.uint16)
+    d2["q_idx"] = qi.cpu().numpy()
+    d2["q"] = qo.view(torch.int16).cpu().numpy().view(np.uint16)
+    app = {"idx_k": d2["k_idx"][Lk - T:], "k": d2["k"][Lk - T:], "v": d2["v"][Lk - T:],
+           "idx_q": d2["q_idx"], "q": d2["q"]}
+    check_append(app, inp, Lk, T)
+    S_ref = oracle.index_scores(d2["q_idx"], d2["w"], d2["k_idx"], Lk, T)
+    idx_ref = oracle.topk(S_ref, Lk, T, cfg.k)
+    idx_gpu = idx.cpu().numpy()
+    for t in range(T):
+        ok, msg = oracle.topk_check(idx_gpu[t], idx_ref[t], S_ref[t, :Lk - T + t + 1], cfg.k)
+        assert ok, f"row {t}: {msg}"
+    o_ref, _ = oracle.sparse_attention(d2["q"], d2["k"], d2["v"], idx_gpu, d2["sink"], float(d2["sm_scale"]))
+    ok, msg = oracle.attn_check(out.float().cpu().numpy(), o_ref)
+    assert ok, msg

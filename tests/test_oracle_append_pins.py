@@ -110,8 +110,8 @@ def test_rope_inner_products_depend_only_on_the_position_difference():
     R, base = 64, 1e4
     q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
     m, n = 1234, 1001
-    lhs = float(ca.rope(q, [m], R, base) @ ca.rope(k, [n], R, base).T)
-    rhs = float(ca.rope(q, [m - n], R, base) @ k.T)
+    lhs = float((ca.rope(q, [m], R, base) @ ca.rope(k, [n], R, base).T).item())
+    rhs = float((ca.rope(q, [m - n], R, base) @ k.T).item())
     assert math.isclose(lhs, rhs, rel_tol=1e-10, abs_tol=1e-10)
 
 
@@ -140,8 +140,8 @@ def test_rope_mutant_with_a_flipped_sign_fails_the_relative_pin():
 
     q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
     m, n = 1234, 1001
-    lhs = float(bad_rope(q, [m], R, base) @ bad_rope(k, [n], R, base).T)
-    rhs = float(bad_rope(q, [m - n], R, base) @ k.T)
+    lhs = float((bad_rope(q, [m], R, base) @ bad_rope(k, [n], R, base).T).item())
+    rhs = float((bad_rope(q, [m - n], R, base) @ k.T).item())
     assert not math.isclose(lhs, rhs, rel_tol=1e-6)
 
 
