@@ -16,6 +16,9 @@ Printed (one JSON line):
   prefill_indexer  the fp8 MFMA contraction of an 8,192-token prefill chunk
             against 1,056,768 keys (causal): achieved TFLOP/s and % of the
             5.0 PFLOP/s dense fp8 peak
+  cache_append     the step that appends new tokens to the caches (LayerNorm,
+            partial RoPE, fp8/bf16 rounding, cache writes): one decode token,
+            and a full 8,192-token prefill chunk as HBM GB/s
   cpu_baseline     the fp64 oracle's decode step on this host, on a bounded
             sample, in the same unit
 """
@@ -58,6 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run 4 plain device copies of this many bytes (calibrates HBM counters)")
@@ -162,6 +166,8 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
 
+    if not args.no_append:
+        result["cache_append"] = bench_append(torch, binding, dev, inst[0], reps)
     if not args.no_prefill:
         del scores
         result["prefill_indexer"] = bench_prefill(torch, np, binding, synth, dev)
@@ -252,6 +258,63 @@ def bench_prefill(torch, np, binding, synth, dev, chunk=1024, reps=2):
             "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "bound": "mfma",
             "score_bytes_written": PREFILL_T * PREFILL_LK * 4}
+
+
+# algorithmic bytes of the append step per new token: bf16 inputs (16 index
+# query heads x 128, the index key, 64 query heads x 192, 4 KV heads x (192 +
+# 128)) read once; fp8 index queries and key, bf16 queries, keys and values
+# written once
+APPEND_READ = 16 * 128 * 2 + 128 * 2 + 64 * 192 * 2 + 4 * 192 * 2 + 4 * 128 * 2
+APPEND_WRITE = 16 * 128 + 128 + 64 * 192 * 2 + 4 * 192 * 2 + 4 * 128 * 2
+APPEND_BYTES_PER_TOKEN = APPEND_READ + APPEND_WRITE               # 60,800
+
+
+def bench_append(torch, binding, dev, x, reps):
+    """dsa_cache_append: one decode token appended to the 1M-token caches
+    (latency), and a full 8,192-token prefill chunk appended at positions
+    1,048,576 .. 1,056,767 (HBM throughput).  Inputs are seeded N(0,1) bf16."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+
+    def acts(T):
+        r = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        return {"idx_q": r(T, 16, 128), "idx_k": r(T, 128), "q": r(T, 64, 192), "k": r(T, 4, 192),
+                "v": r(T, 4, 128), "ln_gamma": 1 + 0.1 * torch.randn(128, generator=gen, device=dev),
+                "ln_beta": 0.1 * torch.randn(128, generator=gen, device=dev)}
+
+    def runner(a, T, Lk, kic, kc, vc):
+        qi = torch.empty((T, 16, 128), dtype=torch.uint8, device=dev)
+        qo = torch.empty((T, 64, 192), dtype=torch.bfloat16, device=dev)
+        return lambda: binding.dsa_cache_append(a["idx_q"], a["idx_k"], a["q"], a["k"], a["v"], Lk, T, kic, kc, vc,
+                                                ln_gamma=a["ln_gamma"], ln_beta=a["ln_beta"], q_idx_out=qi,
+                                                q_out=qo)
+
+    # decode: one token at position LK - 1 of the resident 1M caches
+    one = runner(acts(1), 1, LK, x["k_idx"], x["k"].view(torch.bfloat16), x["v"].view(torch.bfloat16))
+    one()
+    torch.cuda.synchronize()
+    g1 = capture(torch, lambda: [one() for _ in range(16)])
+    us_one = replay_ms(torch, g1, max(reps, 10))[0] / 16 * 1e3
+
+    # prefill chunk: 8,192 tokens
+    T = PREFILL_T
+    Lk = PREFILL_LK
+    kic = torch.zeros((Lk, 128), dtype=torch.uint8, device=dev)
+    kc = torch.zeros((Lk, 4, 192), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((Lk, 4, 128), dtype=torch.bfloat16, device=dev)
+    big = runner(acts(T), T, Lk, kic, kc, vc)
+    big()
+    torch.cuda.synchronize()
+    g8 = capture(torch, lambda: [big() for _ in range(4)])
+    us_big = replay_ms(torch, g8, max(reps // 4, 10))[0] / 4 * 1e3
+    nbytes = T * APPEND_BYTES_PER_TOKEN
+    gbs = nbytes / (us_big * 1e-6) / 1e9
+    del kic, kc, vc
+    return {"kernel": "cache_append_kernel", "decode_t1_us": round(us_one, 3),
+            "prefill": {"workload": "dsa_prefill_1m_t8k append", "tokens": T, "us": round(us_big, 3),
+                        "bytes": nbytes, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"},
+            "bytes_per_token": APPEND_BYTES_PER_TOKEN}
 
 
 def cpu_baseline(d, n_steps):

@@ -18,13 +18,9 @@
 //    (lossless) and multiplied on the bf16 MFMA, whose products are exact and
 //    whose sums are fp32-accurate.  Optionally the kernel also builds the
 //    level-1 radix histogram of its scores for the top-k that follows.
-//  * idx_gemm_kernel (T > 8, prefill): a [T*16 x 128] x [128 x Lk] contraction
-//    on the fp8 MFMA (16x16x128), tiled 32 tokens x 128 keys per workgroup with
-//    an XCD-aware tile order, causal tiles masked, same epilogue.  The fp8
-//    MFMA adds each group of 8 products after aligning them to the group's
-//    largest exponent, so its sums carry less precision than fp32 (measured
-//    and bounded in the tests).
+//  * T > 8 (prefill) goes to idx_gemm_kernel (prefill_scores.hip).
 #include "dsa_common.hpp"
+#include "indexer.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -45,29 +41,6 @@ __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
-}
-
-__device__ __forceinline__ i32x8 load_frag32_cached(const uint8_t* p) {
-  const i32x4* q = reinterpret_cast<const i32x4*>(p);
-  i32x4 lo = q[0];
-  i32x4 hi = q[1];
-  i32x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
-// ReLU-weighted head sum for the key of this lane's column.  c holds heads
-// 4*grp + {0..3}; wv the matching weights.  The two butterflies add the
-// partial sums of the four lane groups; every lane ends with the same bits.
-__device__ __forceinline__ float relu_weighted_sum(const f32x4& c, const float* wv) {
-  float s = wv[0] * fmaxf(c[0], 0.0f);
-  s = fmaf(wv[1], fmaxf(c[1], 0.0f), s);
-  s = fmaf(wv[2], fmaxf(c[2], 0.0f), s);
-  s = fmaf(wv[3], fmaxf(c[3], 0.0f), s);
-  s += shfl_xor_f(s, 16);
-  s += shfl_xor_f(s, 32);
-  return s;
 }
 
 // 32 fp8 bytes -> four bf16x8 MFMA operands (k-step s takes bytes 8s..8s+7)
@@ -403,75 +376,6 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   }
 }
 
-// ---------------------------------------------------------------- prefill
-constexpr int kGemmTok = 32;     // tokens per workgroup (8 per wave)
-constexpr int kGemmKeys = 128;   // keys per workgroup (8 blocks of 16)
-constexpr int kGemmGroupT = 32;  // token tiles per L2 super-tile
-
-__global__ __launch_bounds__(256) void idx_gemm_kernel(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint8_t* __restrict__ k_idx, int64_t Lk, int T, float* __restrict__ scores,
-    int64_t ld, int64_t n_ttiles, int64_t n_ktiles, int64_t per_xcd) {
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
-  // range of logical tiles, ordered so consecutive tiles share a key tile
-  // and a group of token tiles stays resident in that XCD's L2.
-  const int64_t bid = blockIdx.x;
-  const int64_t logical = (bid & 7) * per_xcd + (bid >> 3);
-  const int64_t total = n_ttiles * n_ktiles;
-  if (logical >= total) return;
-  const int64_t gsz = kGemmGroupT * n_ktiles;
-  const int64_t g = logical / gsz;
-  const int64_t rem = logical - g * gsz;
-  const int64_t g_tiles = (g + 1) * kGemmGroupT <= n_ttiles ? kGemmGroupT : n_ttiles - g * kGemmGroupT;
-  const int64_t ktile = rem / g_tiles;
-  const int64_t ttile = g * kGemmGroupT + rem % g_tiles;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int t0 = (int)(ttile * kGemmTok) + wave * 8;
-  const int64_t s0 = ktile * kGemmKeys;
-  if (t0 >= T) return;                                 // wave-uniform
-
-  // this wave's 8 tokens see keys up to p_{t0+7}; skip the MFMAs when every
-  // key of the tile is beyond p_{t0}+... and only write -inf
-  const int64_t pmax = Lk - T + (t0 + 7 < T ? t0 + 7 : T - 1);
-  const bool all_masked = s0 > pmax;
-
-  i32x8 a[8];
-  float wv[8][4];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int t = t0 + j < T ? t0 + j : T - 1;
-    if (!all_masked) a[j] = load_frag32_cached(q_idx + (size_t)(t * 16 + col) * 128 + 32 * grp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[j][i] = w[t * 16 + 4 * grp + i];
-  }
-  const int64_t last = Lk - 1;
-#pragma unroll 1
-  for (int kb = 0; kb < kGemmKeys / 16; ++kb) {
-    const int64_t key = s0 + kb * 16 + col;
-    if (s0 + kb * 16 >= Lk) break;                     // wave-uniform
-    float s[8];
-    if (!all_masked) {
-      const int64_t keyc = key < last ? key : last;
-      i32x8 b = load_frag32_cached(k_idx + keyc * 128 + 32 * grp);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        f32x4 c = mfma_f8_16x16x128(a[j], b, f32x4{0.f, 0.f, 0.f, 0.f});
-        s[j] = relu_weighted_sum(c, wv[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = t0 + j;
-      if (all_masked || key > Lk - T + t) s[j] = -INFINITY;
-      if ((j & 3) == grp && t < T && key < Lk) scores[(int64_t)t * ld + key] = s[j];
-    }
-  }
-}
-
 }  // namespace
 
 int scan_grid(int64_t Lk) {
@@ -532,14 +436,7 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
     return hipGetLastError();
   }
   if (with_hist) return hipErrorInvalidValue;
-  const int64_t n_ttiles = cdiv(T, kGemmTok);
-  const int64_t n_ktiles = cdiv(Lk, kGemmKeys);
-  const int64_t per_xcd = cdiv(n_ttiles * n_ktiles, 8);
-  const int64_t nblocks = per_xcd * 8;
-  if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(idx_gemm_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, q_idx, w, k_idx,
-                     Lk, T, scores, ld, n_ttiles, n_ktiles, per_xcd);
-  return hipGetLastError();
+  return launch_idx_gemm(q_idx, w, k_idx, Lk, T, scores, ld, st);
 }
 
 }  // namespace dsa

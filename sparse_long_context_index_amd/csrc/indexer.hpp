@@ -1,0 +1,65 @@
+// indexer.hpp -- pieces shared by the two lightning-indexer kernels (the
+// decode scan and the prefill contraction): operand loads and the
+// ReLU-weighted head sum of a 16x16 head x key MFMA tile ("Naive-N0.5-Flash:
+// no full-attention layers, and a runtime built by AI", section "Inside a DSA
+// layer: the lightning indexer").
+#pragma once
+
+#include "dsa_common.hpp"
+
+namespace dsa {
+
+__device__ __forceinline__ i32x8 load_frag32_cached(const uint8_t* p) {
+  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+  i32x4 lo = q[0];
+  i32x4 hi = q[1];
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Sum over the four 16-lane rows of the wave, in the order (r0 + r1) + (r2 +
+// r3), on the VALU: permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap
+// the two halves; every lane ends with the same bits.
+__device__ __forceinline__ float sum_rows4(float s) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max(x, 0) on the integer unit: a float whose sign bit is set is a negative
+// int32, every other float keeps its bits (-0.0 becomes +0.0)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// ReLU-weighted head sum for the key of this lane's column.  c holds heads
+// 4*grp + {0..3}; wv the matching weights; the row sum adds the partial sums
+// of the four lane groups.
+__device__ __forceinline__ float relu_weighted_part(const f32x4& c, const float* wv) {
+  float s = wv[0] * relu_bits(c[0]);
+  s = fmaf(wv[1], relu_bits(c[1]), s);
+  s = fmaf(wv[2], relu_bits(c[2]), s);
+  s = fmaf(wv[3], relu_bits(c[3]), s);
+  return s;
+}
+
+__device__ __forceinline__ float relu_weighted_sum(const f32x4& c, const float* wv) {
+  return sum_rows4(relu_weighted_part(c, wv));
+}
+
+// Row sums of four values at once: x[i] holds token i's partial sums in the
+// four rows; the result holds in row r the full sum of token r, added in the
+// order (r0 + r1) + (r2 + r3).  permlane16_swap(a, b) leaves rows (a0, b0, a2,
+// b2) and (a1, b1, a3, b3), permlane32_swap(u, v) leaves (u0, u1, v0, v1) and
+// (u2, u3, v2, v3).
+__device__ __forceinline__ float sum_rows4x4(float x0, float x1, float x2, float x3) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x2), __float_as_uint(x3), false, false);
+  const float u = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace dsa

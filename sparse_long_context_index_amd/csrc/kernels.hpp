@@ -84,6 +84,10 @@ int decode_chunks(int k);
 hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 
 // ---- cache append (LayerNorm / partial RoPE / fp8 of the indexer, RoPE of attention q, k)
+// prefill contraction of the index scores (T > 8)
+hipError_t launch_idx_gemm(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
+                           float* scores, int64_t ld, hipStream_t st);
+
 hipError_t launch_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
                                const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, int64_t Lk, int T, int rot_idx, int rot_main, double base,
