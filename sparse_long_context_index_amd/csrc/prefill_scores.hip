@@ -74,8 +74,9 @@ __device__ __forceinline__ void store_round(const float* st, int64_t rk, int t0,
   float* r1 = scores + (int64_t)(t0 + grp + 4) * ld + key;
   const bool rows16 = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   if (rows16 && rk + kRoundKeys <= Lk && t0 + 8 <= T) {   // wave-uniform
-    *reinterpret_cast<float4*>(r0) = v0;
-    *reinterpret_cast<float4*>(r1) = v1;
+    // streaming stores: the score rows are read back only by a later kernel
+    __builtin_nontemporal_store(f32x4{v0.x, v0.y, v0.z, v0.w}, reinterpret_cast<f32x4*>(r0));
+    __builtin_nontemporal_store(f32x4{v1.x, v1.y, v1.z, v1.w}, reinterpret_cast<f32x4*>(r1));
     return;
   }
   const bool w0 = t0 + grp < T, w1 = t0 + grp + 4 < T;
