@@ -89,7 +89,8 @@ typedef enum dsa_op {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_ATTN = 2,
   DSA_OP_SWA_ATTN = 3,
-  DSA_OP_DECODE_STEP = 4
+  DSA_OP_DECODE_STEP = 4,
+  DSA_OP_PREFILL_TOPK = 5
 } dsa_op;
 
 /*
@@ -200,6 +201,29 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
                            uint16_t* out, float* lse, int32_t* idx_out,
                            float* scores_out, int64_t ld_scores,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_prefill_topk -- dsa_index_scores followed by dsa_topk for many query
+ * rows (the prefill chunk) without writing the [T][Lk] score matrix
+ * ([NoFA] "Inside a DSA layer": every visible key is scored and the top
+ * index_top_k kept; "What 'no full-attention layers' means": a stable
+ * descending argsort).  idx [T][k] int32 receives, per row, the min(k, p_t+1)
+ * best keys by (score desc, index asc) in ascending index order, -1 padded --
+ * the same set, element for element, as dsa_index_scores (T > 8 arithmetic)
+ * then dsa_topk.
+ *
+ * Internally: scores of every 64th key give each row a threshold; one pass of
+ * the fp8 MFMA contraction keeps only keys at or above it (up to 8192 per
+ * row); an exact selection over those follows.  A row whose kept keys do not
+ * fit or number fewer than min(k, p_t+1) is recomputed alone with the same
+ * arithmetic, so the result never depends on the threshold.  The call reads
+ * one word back to learn whether any row needs that (it synchronises
+ * `stream` once and cannot be captured into a graph).
+ * Limits: 1 <= T <= Lk < 2^31, 1 <= k <= 2048.  Needs ws (DSA_OP_PREFILL_TOPK,
+ * about T * (Lk / 16 + 64 KiB) bytes).
+ */
+dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int32_t T,
+                            int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dsa_cache_append -- the step before the index sweep for T new tokens at

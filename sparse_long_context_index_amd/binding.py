@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 DSA_OK = 0
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
           4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP = range(5)
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK = range(6)
 
 IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
 ROPE_BASE = 1.0e7          # DSA_ROPE_BASE
@@ -45,6 +45,7 @@ _SIGS = {
                          _P, _SZ, _P], _I32),
     "dsa_cache_append": ([_P, _P, _P, _P, _F, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
                           _P, _P, _P, _P, _P, _P], _I32),
+    "dsa_prefill_topk": ([_P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "dsa_workspace_bytes": ([_I32, _I64, _I32, _I32, _I32], _SZ),
     "dsa_workspace_init": ([_P, _SZ, _P], _I32),
     "dsa_status_string": ([_I32], ctypes.c_char_p),
@@ -142,6 +143,16 @@ def dsa_topk(scores, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] 
     ws = (ws or Workspace(device=scores.device)).ensure(workspace_bytes(OP_TOPK, Lk, T, k))
     _check(load().dsa_topk(_dev(scores, "scores"), ld, Lk, T, k, _dev(idx, "idx"), ws.ptr, ws.nbytes,
                            _stream()), "dsa_topk")
+    return idx
+
+
+def dsa_prefill_topk(q_idx, w, k_idx, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] = None):
+    """Index scores and per-row top-k of T query rows without the score matrix."""
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_idx.device)
+    ws = (ws or Workspace(device=q_idx.device)).ensure(workspace_bytes(OP_PREFILL_TOPK, Lk, T, k))
+    _check(load().dsa_prefill_topk(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), Lk, T, k,
+                                   _dev(idx, "idx"), ws.ptr, ws.nbytes, _stream()), "dsa_prefill_topk")
     return idx
 
 

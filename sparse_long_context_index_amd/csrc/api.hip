@@ -2,6 +2,7 @@
 // workspace carving and launch sequencing.  Every check happens before the
 // first launch, so a rejected call enqueues nothing and touches no output.
 #include <cmath>
+#include <vector>
 
 #include "dsa_common.hpp"
 #include "kernels.hpp"
@@ -84,6 +85,34 @@ DecodeLayout decode_layout(int64_t Lk, int T, int k) {
   return d;
 }
 
+// workspace of the fused prefill top-k
+struct PrefillLayout {
+  size_t sample, theta, count, failed, cand, fb, topk, total;
+  int64_t ld_sample;
+};
+
+PrefillLayout prefill_layout(int64_t Lk, int T) {
+  PrefillLayout d;
+  d.ld_sample = (cdiv(Lk, kPrefillStep) + 3) / 4 * 4;
+  size_t off = kCounterRegionBytes;            // the fallback top-k's counters
+  d.sample = off;
+  off += align_up((size_t)T * d.ld_sample * sizeof(float));
+  d.theta = off;
+  off += align_up((size_t)T * sizeof(uint32_t));
+  d.count = off;                               // T row counters, then the failure count
+  off += align_up(((size_t)T + 4) * sizeof(uint32_t));
+  d.failed = off;
+  off += align_up((size_t)T * sizeof(uint32_t));
+  d.cand = off;
+  off += align_up((size_t)T * kPrefillCap * sizeof(uint2));
+  d.fb = off;
+  off += align_up((size_t)Lk * sizeof(float));
+  d.topk = off;
+  off += align_up(topk_scratch_bytes(Lk, 1, DSA_TOPK_MAX));
+  d.total = off;
+  return d;
+}
+
 }  // namespace
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
@@ -132,6 +161,9 @@ size_t dsa_workspace_bytes(dsa_op op, int64_t Lk, int32_t T, int32_t k, int32_t 
     case DSA_OP_DECODE_STEP:
       if (T < 1 || T > DSA_DECODE_T_MAX || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
       return decode_layout(Lk, T, k).total;
+    case DSA_OP_PREFILL_TOPK:
+      if (T < 1 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
+      return prefill_layout(Lk, T).total;
   }
   return 0;
 }
@@ -274,6 +306,54 @@ dsa_status dsa_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const 
   return hip_status(launch_cache_append(idx_q, idx_k, ln_gamma, ln_beta, ln_eps, q, k, v, Lk, T, rot_idx,
                                         rot_main, rope_base, q_idx_out, k_idx_cache, q_out, k_cache, v_cache,
                                         as_stream(stream)));
+}
+
+dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int32_t T,
+                            int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_index_args(q_idx, w, k_idx, Lk, T);
+  if (s != DSA_OK) return s;
+  if (!idx) return DSA_ERR_NULL;
+  if (!aligned16(idx)) return DSA_ERR_ALIGN;
+  if (k < 1 || k > DSA_TOPK_MAX) return DSA_ERR_SHAPE;
+  const PrefillLayout d = prefill_layout(Lk, T);
+  if (!ws || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* sample = reinterpret_cast<float*>(base + d.sample);
+  uint32_t* theta = reinterpret_cast<uint32_t*>(base + d.theta);
+  uint32_t* count = reinterpret_cast<uint32_t*>(base + d.count);
+  uint32_t* nfail = count + T;
+  uint32_t* failed = reinterpret_cast<uint32_t*>(base + d.failed);
+  const PrefillCand pc{theta, count, reinterpret_cast<uint2*>(base + d.cand), kPrefillCap};
+  hipError_t e = launch_zero(count, align_up(((size_t)T + 4) * sizeof(uint32_t)), st);
+  if (e == hipSuccess) e = launch_idx_gemm_sample(q_idx, w, k_idx, Lk, T, kPrefillStep, sample, d.ld_sample, st);
+  if (e == hipSuccess) e = launch_prefill_theta(sample, d.ld_sample, Lk, T, kPrefillStep, k, kPrefillCap, theta, st);
+  if (e == hipSuccess) e = launch_idx_gemm_cand(q_idx, w, k_idx, Lk, T, pc, st);
+  if (e == hipSuccess) e = launch_prefill_refine(pc, Lk, T, k, idx, nfail, failed, st);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  // rows whose candidates did not fit or were too few: recompute each with the
+  // same contraction over its visible keys and the row top-k
+  uint32_t nf = 0;
+  if (hipMemcpyAsync(&nf, nfail, sizeof(nf), hipMemcpyDeviceToHost, st) != hipSuccess) return DSA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return DSA_ERR_HIP;
+  if (nf == 0) return DSA_OK;
+  if (nf > (uint32_t)T) return DSA_ERR_HIP;
+  std::vector<uint32_t> rows(nf);
+  if (hipMemcpyAsync(rows.data(), failed, nf * sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DSA_ERR_HIP;
+  float* fb = reinterpret_cast<float*>(base + d.fb);
+  for (uint32_t t : rows) {
+    if (t >= (uint32_t)T) return DSA_ERR_HIP;
+    const int64_t nvis = Lk - T + t + 1;
+    e = launch_idx_gemm(q_idx + (size_t)t * DSA_IDX_HEADS * DSA_IDX_DIM, w + (size_t)t * DSA_IDX_HEADS, k_idx, nvis, 1,
+                        fb, nvis, st);
+    if (e == hipSuccess)
+      e = launch_topk(fb, nvis, nvis, 1, k, idx + (size_t)t * k, ws, base + d.topk, st);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
 }
 
 }  // extern "C"

@@ -83,11 +83,37 @@ struct DecodeArgs {
 int decode_chunks(int k);
 hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 
-// ---- cache append (LayerNorm / partial RoPE / fp8 of the indexer, RoPE of attention q, k)
-// prefill contraction of the index scores (T > 8)
+// ---- prefill contraction of the index scores (T > 8; any T >= 1 works)
 hipError_t launch_idx_gemm(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                            float* scores, int64_t ld, hipStream_t st);
+// scores of the sampled keys 0, step, 2 step, ...: column j of a row is key j * step
+hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
+                                  int step, float* scores, int64_t ld, hipStream_t st);
+// candidate emission: every visible key whose order key reaches theta[t] is
+// appended to row t's slots as (order key, index); count[t] counts them all
+// (slots past cap are not written)
+struct PrefillCand {
+  const uint32_t* theta;   // [T]
+  uint32_t* count;         // [T], zero before the launch
+  uint2* cand;             // [T][cap]
+  int cap;
+};
+hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
+                                const PrefillCand& pc, hipStream_t st);
 
+// ---- fused prefill top-k (prefill_topk.hip)
+constexpr int kPrefillStep = 64;           // key sample stride of the threshold estimate
+constexpr int kPrefillCap = 8192;          // candidate slots per row
+size_t prefill_refine_lds(int cap);
+// theta[t]: order key of the row's threshold (0: every visible key)
+hipError_t launch_prefill_theta(const float* sample, int64_t ld, int64_t Lk, int T, int step, int k, int cap,
+                                uint32_t* theta, hipStream_t st);
+// exact top-k of each row from its candidates into idx [T][k]; rows whose
+// candidates do not fit or are too few are appended to failed (nfail counts)
+hipError_t launch_prefill_refine(const PrefillCand& pc, int64_t Lk, int T, int k, int32_t* idx, uint32_t* nfail,
+                                 uint32_t* failed, hipStream_t st);
+
+// ---- cache append (LayerNorm / partial RoPE / fp8 of the indexer, RoPE of attention q, k)
 hipError_t launch_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
                                const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, int64_t Lk, int T, int rot_idx, int rot_main, double base,

@@ -149,3 +149,28 @@ def test_cache_append_validation(L):
     assert call(base=0.0) == 2
     assert call(base=float("nan")) == 2
     assert call(eps=-1.0) == 2
+
+
+def test_prefill_topk_validation(L):
+    f = L.dsa_prefill_topk
+    ws_need = L.dsa_workspace_bytes(binding.OP_PREFILL_TOPK, 100000, 64, 2048, 0)
+    assert ws_need > 64 * 8192 * 8                      # the candidate slots alone
+    assert L.dsa_workspace_bytes(binding.OP_PREFILL_TOPK, 100000, 64, 0, 0) == 0
+    assert L.dsa_workspace_bytes(binding.OP_PREFILL_TOPK, 100000, 64, 2049, 0) == 0
+    assert L.dsa_workspace_bytes(binding.OP_PREFILL_TOPK, 10, 64, 16, 0) == 0     # Lk < T
+    # a workspace sized for larger sizes serves smaller ones
+    assert L.dsa_workspace_bytes(binding.OP_PREFILL_TOPK, 50000, 32, 7, 0) <= ws_need
+
+    def call(q=A, w=A, k=A, Lk=100000, T=64, kk=2048, idx=A, ws=A, nb=ws_need):
+        return f(q, w, k, Lk, T, kk, idx, ws, nb, None)
+    assert call(q=None) == 1
+    assert call(idx=None) == 1
+    assert call(idx=MIS) == 4
+    assert call(k=MIS) == 4
+    assert call(T=0) == 2
+    assert call(Lk=10) == 2
+    assert call(kk=0) == 2
+    assert call(kk=2049) == 2
+    assert call(ws=None) == 5
+    assert call(nb=ws_need - 1) == 5
+    assert call(ws=MIS) == 4
