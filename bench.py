@@ -37,6 +37,7 @@ ROTATE = 4
 
 # algorithmic bytes of one dsa_decode_1m step
 L, T, K = 1048576, 1, 2048
+K_TOP = K
 LK = L + T
 BYTES_KEYS = LK * 128
 BYTES_GATHER = K * 4 * (192 + 128) * 2
@@ -62,6 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-batch", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run 4 plain device copies of this many bytes (calibrates HBM counters)")
@@ -168,6 +170,8 @@ def main():
 
     if not args.no_append:
         result["cache_append"] = bench_append(torch, binding, dev, inst[0], reps)
+    if not args.no_batch:
+        result["decode_batch"] = bench_batch(torch, np, binding, synth, dev, reps)
     if not args.no_prefill:
         del scores
         result["prefill_indexer"] = bench_prefill(torch, np, binding, synth, dev)
@@ -332,6 +336,40 @@ def bench_append(torch, binding, dev, x, reps):
                         "bytes": nbytes, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"},
             "bytes_per_token": APPEND_BYTES_PER_TOKEN}
+
+
+def bench_batch(torch, np, binding, synth, dev, reps, B=64):
+    """dsa_decode_batch: 64 sequences with key counts uniform in [256, 65536]
+    (one new token each) sharing one cache; seeded N(0,1) inputs drawn on the
+    device.  Algorithmic bytes: every sequence's index keys, the gathered K/V
+    of its min(k, keys) selected rows, and its query, output and weights."""
+    lens = synth.batch_lengths(B, 256, 65536, seed=1005)
+    n_rows = int(lens.sum())
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(41)
+    f8 = lambda *sh: torch.randn(sh, generator=gen, device=dev).to(torch.float8_e4m3fn).view(torch.uint8)
+    bf = lambda *sh: torch.randn(sh, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    k_idx, K, V = f8(n_rows, 128), bf(n_rows, 4, 192), bf(n_rows, 4, 128)
+    q_idx, q = f8(B, 1, 16, 128), bf(B, 1, 64, 192)
+    w = torch.randn((B, 1, 16), generator=gen, device=dev)
+    sink = torch.randn((64,), generator=gen, device=dev)
+    st = torch.from_numpy(starts).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    max_len = int(lens.max())
+    ws = binding.Workspace(binding.workspace_bytes(binding.OP_DECODE_BATCH, max_len, 1, K_TOP, B))
+    out = torch.empty((B, 1, 64, 128), dtype=torch.bfloat16, device=dev)
+    call = lambda: binding.dsa_decode_batch(q_idx, w, k_idx, q, K, V, st, sl, max_len, K_TOP, sink,
+                                            1.0 / 192 ** 0.5, out=out, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [call() for _ in range(4)])
+    us = replay_ms(torch, g, max(reps // 4, 10))[0] / 4 * 1e3
+    nbytes = int((lens * 128).sum() + (np.minimum(lens, K_TOP) * 4 * 320 * 2).sum()) + B * (2048 + 64 + 24576 + 16384)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "dsa_decode_batch b64 lengths U[256,65536] T=1 k=2048", "us": round(us, 3),
+            "tokens_per_s": round(B / (us * 1e-6), 1), "bytes": nbytes, "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
 def cpu_baseline(d, n_steps):

@@ -7,19 +7,23 @@
  *   [NoFA]   "Naive-N0.5-Flash: no full-attention layers, and a runtime built
  *            by AI" (ai.thesatyajit.com) -- property table; section "What 'no
  *            full-attention layers' means"; section "Inside a DSA layer: the
- *            lightning indexer" and its Figure 1; section "How much of this
- *            did AI actually build?".
+ *            lightning indexer" and its Figure 1; section "The runtime is the
+ *            actual claim"; section "How much of this did AI actually build?".
  *   [Master] "Naive-N0.5-Flash: the open-weight 309B MoE with no full-attention
  *            layers at all aims for 2,000 tokens/s per user" (ai-master.dev),
  *            section "Zero full-attention: what it really changes".
+ *   [Reading] "2,122 tok/s, Zero Full-Attention Layers: Reading
+ *            Naive-N0.5-Flash Carefully" (sheldonwangrjt.github.io), section
+ *            "The 42x footnote".
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless a
  *   parameter says otherwise.  `stream` is a hipStream_t passed as void*; NULL
- *   means the default stream.  Every call only enqueues work on `stream` and
- *   returns without synchronising; outputs are ready when the stream reaches
- *   that point.
+ *   means the default stream.  Every call except dsa_prefill_topk only
+ *   enqueues work on `stream` and returns without synchronising; outputs are
+ *   ready when the stream reaches that point.  dsa_prefill_topk waits for
+ *   `stream` once, to read back how many rows need its exact fallback.
  * - Ownership: the caller owns every buffer.  The library never allocates or
  *   frees memory on a call path and keeps no global mutable state.  Scratch
  *   space is the caller's workspace `ws` of at least dsa_workspace_bytes()
@@ -90,7 +94,8 @@ typedef enum dsa_op {
   DSA_OP_SPARSE_ATTN = 2,
   DSA_OP_SWA_ATTN = 3,
   DSA_OP_DECODE_STEP = 4,
-  DSA_OP_PREFILL_TOPK = 5
+  DSA_OP_PREFILL_TOPK = 5,
+  DSA_OP_DECODE_BATCH = 6
 } dsa_op;
 
 /*
@@ -201,6 +206,37 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
                            uint16_t* out, float* lse, int32_t* idx_out,
                            float* scores_out, int64_t ld_scores,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode_batch -- dsa_decode_step for B sequences of different lengths
+ * at once, T query tokens each (serving many users, T = 1: [Reading] "The
+ * 42x footnote" on the Standard-mode figure; the verify step of a
+ * speculative round, T up to 16: [NoFA] "The runtime is the actual claim").  The sequences share one index-key cache and one K/V
+ * cache: sequence b owns rows seq_start[b] .. seq_start[b] + seq_len[b] - 1,
+ * its history followed by its T new tokens, so its token t sits at position
+ * seq_len[b] - T + t and sees the sequence's keys 0 .. seq_len[b] - T + t.
+ *
+ *   q_idx [B][T][16][128] fp8, w [B][T][16] f32, q [B][T][64][192] bf16
+ *   k_idx [n_rows][128] fp8, k_cache [n_rows][4][192], v_cache [n_rows][4][128] bf16
+ *   seq_start [B] int64, seq_len [B] int32   (device arrays)
+ *   max_len   an upper bound of every seq_len (sizes the workspace)
+ *   out [B][T][64][128] bf16, lse [B][T][64] f32 (optional)
+ *   idx_out   [B][T][k] int32 (optional): positions within each sequence,
+ *             ascending, -1 padded
+ *
+ * Each row's selection is the top-k rule of dsa_topk over its own scores,
+ * and its attention that of sparse_gqa_attn over the selected rows.  A
+ * sequence with seq_len outside [0, max_len] or rows outside [0, n_rows) is
+ * treated as empty (its outputs are those of an empty selection).  T <= 8
+ * takes the streaming scan per sequence, larger T the fp8 contraction.
+ * Limits: 1 <= B <= 65535, 1 <= T <= 16, T <= max_len < 2^31, n_rows < 2^31,
+ * 1 <= k <= 2048.  Needs ws (DSA_OP_DECODE_BATCH with Lk = max_len).
+ */
+dsa_status dsa_decode_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                            const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_rows,
+                            const int64_t* seq_start, const int32_t* seq_len, int32_t B, int32_t T,
+                            int64_t max_len, int32_t k, const float* sink, float sm_scale, uint16_t* out,
+                            float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dsa_prefill_topk -- dsa_index_scores followed by dsa_topk for many query

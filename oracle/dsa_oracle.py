@@ -258,6 +258,13 @@ def dsa_decode_step(inp: dict, k: int, sink=True):
     return S, idx, out, lse
 
 
+def dsa_decode_batch(seqs: list, k: int, sink=True):
+    """Decode step of several sequences: each is its own DSA decode step over
+    its own keys (sharing a cache is storage, not arithmetic), so the batch is
+    the list of per-sequence steps."""
+    return [dsa_decode_step(s, k, sink) for s in seqs]
+
+
 # --------------------------------------------------------------------------
 # Acceptance helpers (tolerances from the arithmetic; used by the tests).
 # --------------------------------------------------------------------------

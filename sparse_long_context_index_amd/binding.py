@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 DSA_OK = 0
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
           4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK = range(6)
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK, OP_DECODE_BATCH = range(7)
 
 IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
 ROPE_BASE = 1.0e7          # DSA_ROPE_BASE
@@ -46,6 +46,8 @@ _SIGS = {
     "dsa_cache_append": ([_P, _P, _P, _P, _F, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
                           _P, _P, _P, _P, _P, _P], _I32),
     "dsa_prefill_topk": ([_P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "dsa_decode_batch": ([_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32, _P, _F, _P, _P, _P,
+                          _P, _SZ, _P], _I32),
     "dsa_workspace_bytes": ([_I32, _I64, _I32, _I32, _I32], _SZ),
     "dsa_workspace_init": ([_P, _SZ, _P], _I32),
     "dsa_status_string": ([_I32], ctypes.c_char_p),
@@ -144,6 +146,22 @@ def dsa_topk(scores, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] 
     _check(load().dsa_topk(_dev(scores, "scores"), ld, Lk, T, k, _dev(idx, "idx"), ws.ptr, ws.nbytes,
                            _stream()), "dsa_topk")
     return idx
+
+
+def dsa_decode_batch(q_idx, w, k_idx, q, k_cache, v_cache, seq_start, seq_len, max_len: int, k: int, sink,
+                     sm_scale: float, out=None, lse=None, idx_out=None, ws: Optional[Workspace] = None):
+    """Decode step of B ragged sequences sharing one cache; q_idx [B,T,16,128]."""
+    B, T = int(q_idx.shape[0]), int(q_idx.shape[1])
+    n_rows = int(k_idx.shape[0])
+    if out is None:
+        out = torch.empty((B, T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
+    ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_DECODE_BATCH, max_len, T, k, B))
+    _check(load().dsa_decode_batch(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), n_rows,
+                                   _dev(seq_start, "seq_start"), _dev(seq_len, "seq_len"), B, T, max_len, k,
+                                   _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
+                                   _dev(idx_out, "idx_out"), ws.ptr, ws.nbytes, _stream()), "dsa_decode_batch")
+    return out
 
 
 def dsa_prefill_topk(q_idx, w, k_idx, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] = None):

@@ -113,6 +113,31 @@ PrefillLayout prefill_layout(int64_t Lk, int T) {
   return d;
 }
 
+// workspace of the batched decode step
+struct BatchLayout {
+  size_t scores, idx, rows, attn, total;
+  int64_t ld;
+};
+
+BatchLayout batch_layout(int64_t max_len, int T, int k, int B) {
+  BatchLayout d;
+  d.ld = (max_len + 3) / 4 * 4;
+  const size_t R = (size_t)B * T;
+  size_t off = kCounterRegionBytes;
+  d.scores = off;
+  off += align_up(R * d.ld * sizeof(float));
+  d.idx = off;
+  off += align_up(R * k * sizeof(int32_t));
+  d.rows = off;
+  off += align_up(R * k * sizeof(int32_t));
+  d.attn = off;
+  off += align_up(attn_scratch_bytes((int)R, k, DSA_KV_HEADS));
+  d.total = off;
+  return d;
+}
+
+constexpr int kBatchTMax = 16;
+
 }  // namespace
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
@@ -161,6 +186,11 @@ size_t dsa_workspace_bytes(dsa_op op, int64_t Lk, int32_t T, int32_t k, int32_t 
     case DSA_OP_DECODE_STEP:
       if (T < 1 || T > DSA_DECODE_T_MAX || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
       return decode_layout(Lk, T, k).total;
+    case DSA_OP_DECODE_BATCH:
+      if (B < 1 || B > 65535 || T < 1 || T > kBatchTMax || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX ||
+          (int64_t)B * T > 0x7FFFFFFF)
+        return 0;
+      return batch_layout(Lk, T, k, B).total;
     case DSA_OP_PREFILL_TOPK:
       if (T < 1 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
       return prefill_layout(Lk, T).total;
@@ -306,6 +336,53 @@ dsa_status dsa_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const 
   return hip_status(launch_cache_append(idx_q, idx_k, ln_gamma, ln_beta, ln_eps, q, k, v, Lk, T, rot_idx,
                                         rot_main, rope_base, q_idx_out, k_idx_cache, q_out, k_cache, v_cache,
                                         as_stream(stream)));
+}
+
+dsa_status dsa_decode_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                            const uint16_t* k_cache, const uint16_t* v_cache, int64_t n_rows,
+                            const int64_t* seq_start, const int32_t* seq_len, int32_t B, int32_t T,
+                            int64_t max_len, int32_t k, const float* sink, float sm_scale, uint16_t* out,
+                            float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_idx || !w || !k_idx || !seq_start || !seq_len) return DSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(seq_start) || !aligned16(seq_len))
+    return DSA_ERR_ALIGN;
+  dsa_status s = check_attn_args(q, k_cache, v_cache, out, sink, lse, sm_scale);
+  if (s != DSA_OK) return s;
+  if (idx_out && !aligned16(idx_out)) return DSA_ERR_ALIGN;
+  if (B < 1 || B > 65535 || T < 1 || T > kBatchTMax || max_len < T || max_len >= kMaxLk || n_rows < 1 ||
+      n_rows >= kMaxLk || k < 1 || k > DSA_TOPK_MAX)
+    return DSA_ERR_SHAPE;
+  const BatchLayout d = batch_layout(max_len, T, k, B);
+  if (!ws || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + d.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx);
+  int32_t* rows = reinterpret_cast<int32_t*>(base + d.rows);
+  SeqBatch sb;
+  sb.start = seq_start;
+  sb.len = seq_len;
+  sb.n_rows = n_rows;
+  sb.max_len = max_len;
+  hipError_t e = launch_index_scores_batch(q_idx, w, k_idx, sb, B, T, scores, d.ld, st);
+  if (e == hipSuccess) e = launch_topk_batch(scores, d.ld, sb, B, T, k, idx, rows, st);
+  if (e == hipSuccess) {
+    AttnArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.n_rows = n_rows;
+    a.idx = rows;
+    a.k_len = k;
+    a.T = B * T;
+    a.sink = sink;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.lse = lse;
+    e = launch_sparse_attn(a, base + d.attn, st);
+  }
+  return hip_status(e);
 }
 
 dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int32_t T,

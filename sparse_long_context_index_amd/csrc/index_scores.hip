@@ -203,7 +203,19 @@ template <int T, bool kLists>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
-    int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist, ScanLists lists) {
+    int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist, ScanLists lists, SeqBatch sb) {
+  if (!kLists && sb.len) {
+    // batch: grid dimension y is the sequence; its keys, queries and score rows
+    const int b = blockIdx.y;
+    int64_t first;
+    Lk = seq_keys(sb, b, &first);
+    q_idx += (size_t)b * T * 16 * 128;
+    w += (size_t)b * T * 16;
+    k_idx += first * 128;
+    scores += (size_t)b * T * ld;
+    ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
+    if (Lk == 0) return;
+  }
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
@@ -423,10 +435,10 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
   case n:                                                                                                   \
     if (with_lists)                                                                                         \
       hipLaunchKernelGGL((idx_scan_kernel<n, true>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,    \
-                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists);                            \
+                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});                \
     else                                                                                                    \
       hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,   \
-                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists);                            \
+                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});                \
     break;
       DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
       DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
@@ -437,6 +449,31 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
   }
   if (with_hist) return hipErrorInvalidValue;
   return launch_idx_gemm(q_idx, w, k_idx, Lk, T, scores, ld, st);
+}
+
+hipError_t launch_index_scores_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const SeqBatch& sb,
+                                     int B, int T, float* scores, int64_t ld, hipStream_t st) {
+  if (B < 1 || T < 1 || ld < sb.max_len || B > 65535) return hipErrorInvalidValue;
+  if (T > kDecodeTMax) return launch_idx_gemm_batch(q_idx, w, k_idx, sb, B, T, scores, ld, st);
+  // per sequence a share of the plain scan's workgroups, at most its key groups
+  const int64_t max_groups = cdiv(cdiv(sb.max_len, 16), 4 * kScanUnroll);
+  int64_t per = cdiv(kPlainScanBlocks, B);
+  per = per < max_groups ? per : max_groups;
+  per = per < 1 ? 1 : per;
+  const size_t lds = scan_lds_bytes(sb.max_len, T, false);
+  const TopkCounters ctr{};
+  switch (T) {
+#define DSA_SCAN_BATCH(n)                                                                                   \
+  case n:                                                                                                   \
+    hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)per, (unsigned)B), dim3(256), lds, st, q_idx, \
+                       w, k_idx, sb.max_len, scores, ld, max_groups, ctr, 0, ScanLists{}, sb);              \
+    break;
+    DSA_SCAN_BATCH(1) DSA_SCAN_BATCH(2) DSA_SCAN_BATCH(3) DSA_SCAN_BATCH(4)
+    DSA_SCAN_BATCH(5) DSA_SCAN_BATCH(6) DSA_SCAN_BATCH(7) DSA_SCAN_BATCH(8)
+#undef DSA_SCAN_BATCH
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -13,6 +13,26 @@ constexpr int kTopkMultiRowsMax = 8;      // rows handled by the multi-block top
 
 constexpr int kListM = 32;                // per-workgroup local top list of the decode scan
 
+// A batch of ragged sequences over shared caches: sequence b owns cache rows
+// start[b] .. start[b] + len[b] - 1 (its history and its T new tokens).  A
+// sequence whose length lies outside [0, max_len] or whose rows leave
+// [0, n_rows) is treated as empty.
+struct SeqBatch {
+  const int64_t* start = nullptr;   // [B] device
+  const int32_t* len = nullptr;     // [B] device
+  int64_t n_rows = 0;
+  int64_t max_len = 0;
+};
+
+// keys of sequence b (0 when its descriptor is invalid); *first receives its first row
+__device__ __forceinline__ int64_t seq_keys(const SeqBatch& sb, int b, int64_t* first) {
+  const int64_t s = sb.start[b];
+  const int64_t n = sb.len[b];
+  const bool ok = n >= 0 && n <= sb.max_len && s >= 0 && s + n <= sb.n_rows;
+  *first = ok ? s : 0;
+  return ok ? n : 0;
+}
+
 // ---- index scores
 // Per-workgroup local top lists of the decode scan.  Entry j of workgroup b's
 // list for row t sits at [(t * kListM + j) * scan_grid + b]; entries are in
@@ -31,6 +51,11 @@ size_t scan_lds_bytes(int64_t Lk, int T, bool lists);   // dynamic LDS of the de
 hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
                                int64_t Lk, int T, float* scores, int64_t ld, hipStream_t st,
                                void* topk_counters = nullptr, ScanLists lists = ScanLists{});
+// scores of B sequences at once: q_idx [B][T][16][128], w [B][T][16], scores
+// [B][T][ld] (ld >= max_len); row (b, t) sees keys 0 .. len[b] - T + t of its
+// sequence.  T <= 8 takes the streaming scan, larger T the contraction.
+hipError_t launch_index_scores_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const SeqBatch& sb,
+                                     int B, int T, float* scores, int64_t ld, hipStream_t st);
 
 // ---- top-k
 size_t topk_scratch_bytes(int64_t Lk, int T, int k);
@@ -39,6 +64,10 @@ bool topk_multi_block(int64_t Lk, int T);   // few long rows: the multi-block pa
 // region (built by the scan); otherwise launch_topk builds it first.
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
                        void* ws_counters, void* scratch, hipStream_t st, bool hist_ready = false);
+// top-k of the B * T rows of a batch ([B][T][ld] scores): idx [B][T][k]
+// positions within each sequence, idx_rows the same as cache rows (-1 kept)
+hipError_t launch_topk_batch(const float* scores, int64_t ld, const SeqBatch& sb, int B, int T, int k, int32_t* idx,
+                             int32_t* idx_rows, hipStream_t st);
 
 // ---- gathered attention
 struct AttnArgs {
@@ -86,6 +115,9 @@ hipError_t launch_decode_attend(const DecodeArgs& d, hipStream_t st);
 // ---- prefill contraction of the index scores (T > 8; any T >= 1 works)
 hipError_t launch_idx_gemm(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                            float* scores, int64_t ld, hipStream_t st);
+// the same for the B sequences of a batch (grid dimension y = sequence)
+hipError_t launch_idx_gemm_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const SeqBatch& sb,
+                                 int B, int T, float* scores, int64_t ld, hipStream_t st);
 // scores of the sampled keys 0, step, 2 step, ...: column j of a row is key j * step
 hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                                   int step, float* scores, int64_t ld, hipStream_t st);

@@ -160,6 +160,7 @@ struct GemmArgs {
   float* scores;       // score modes: [T][ld], column j = key j of the key space
   int64_t ld;
   PrefillCand cand;    // candidate mode
+  SeqBatch sb;         // batch (score mode): grid dimension y is the sequence
   int64_t n_ttiles, n_ktiles, per_xcd;
 };
 
@@ -180,8 +181,19 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
   const int64_t ttile = g * kGemmGroupT + rem % g_tiles;
 
   const int T = ga.T;
-  const int64_t Lk = ga.Lk;
+  int64_t Lk = ga.Lk;
   const int step = kMode == kGemmSample ? ga.step : 1;
+  if (kMode == kGemmScores && ga.sb.len) {
+    const int b = blockIdx.y;
+    int64_t first;
+    Lk = seq_keys(ga.sb, b, &first);
+    ga.q_idx += (size_t)b * T * 16 * 128;
+    ga.w += (size_t)b * T * 16;
+    ga.k_idx += first * 128;
+    ga.scores += (size_t)b * T * ga.ld;
+    ga.nkeys = Lk;
+    if (Lk == 0) return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -290,10 +302,10 @@ GemmArgs gemm_args(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, i
 }
 
 template <int kMode>
-hipError_t launch_gemm(const GemmArgs& ga, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& ga, hipStream_t st, int batch = 1) {
   const int64_t nblocks = ga.per_xcd * 8;
   if (nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(idx_gemm_kernel<kMode>, dim3((unsigned)nblocks), dim3(256), 0, st, ga);
+  hipLaunchKernelGGL(idx_gemm_kernel<kMode>, dim3((unsigned)nblocks, (unsigned)batch), dim3(256), 0, st, ga);
   return hipGetLastError();
 }
 
@@ -305,6 +317,16 @@ hipError_t launch_idx_gemm(const uint8_t* q_idx, const float* w, const uint8_t* 
   ga.scores = scores;
   ga.ld = ld;
   return launch_gemm<kGemmScores>(ga, st);
+}
+
+hipError_t launch_idx_gemm_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const SeqBatch& sb,
+                                 int B, int T, float* scores, int64_t ld, hipStream_t st) {
+  if (B < 1 || B > 65535 || ld < sb.max_len) return hipErrorInvalidValue;
+  GemmArgs ga = gemm_args(q_idx, w, k_idx, sb.max_len, T, 1);
+  ga.scores = scores;
+  ga.ld = ld;
+  ga.sb = sb;
+  return launch_gemm<kGemmScores>(ga, st, B);
 }
 
 hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,

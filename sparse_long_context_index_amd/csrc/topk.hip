@@ -364,13 +364,18 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
 
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                                int64_t Lk, int T, int k,
-                                                               int32_t* __restrict__ idx) {
+                                                               int32_t* __restrict__ idx, SeqBatch sb,
+                                                               int32_t* __restrict__ idx_rows) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint2 cand[kRowCap];
   __shared__ FinalShared fs;
   __shared__ uint32_t s_b1, s_above1;
   const int t = blockIdx.x;
-  const int64_t n = Lk - T + t + 1;
+  int64_t first = 0;
+  if (sb.len) Lk = seq_keys(sb, t / T, &first);        // batch: row t is token t % T of sequence t / T
+  const int tt = sb.len ? t % T : t;
+  int64_t n = Lk - T + tt + 1;
+  n = n > 0 ? n : 0;
   const bool all_mode = n <= (int64_t)k;
   const float* row = scores + (int64_t)t * ld;
   int32_t* out_row = idx + (size_t)t * k;
@@ -422,6 +427,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     RowSource src{row, n, seg, kRowThreads, all_mode ? 0u : b1};
     final_select<kRowThreads>(src, k, all_mode, b1, k1, hist, fs, out_row);
   }
+  if (idx_rows) {
+    // the same set as cache rows of the sequence
+    __syncthreads();
+    for (int j = threadIdx.x; j < k; j += kRowThreads) {
+      const int32_t v = out_row[j];
+      idx_rows[(size_t)t * k + j] = v >= 0 ? (int32_t)(first + v) : -1;
+    }
+  }
 }
 
 bool multi_block(int64_t Lk, int T) {
@@ -441,7 +454,8 @@ size_t topk_scratch_bytes(int64_t Lk, int T, int k) {
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
                        void* ws_counters, void* scratch, hipStream_t st, bool hist_ready) {
   if (!multi_block(Lk, T)) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(T), dim3(kRowThreads), 0, st, scores, ld, Lk, T, k, idx);
+    hipLaunchKernelGGL(topk_row_kernel, dim3(T), dim3(kRowThreads), 0, st, scores, ld, Lk, T, k, idx, SeqBatch{},
+                       (int32_t*)nullptr);
     return hipGetLastError();
   }
   TopkCounters ctr = counters_at(ws_counters);
@@ -466,5 +480,14 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k
 }
 
 bool topk_multi_block(int64_t Lk, int T) { return multi_block(Lk, T); }
+
+hipError_t launch_topk_batch(const float* scores, int64_t ld, const SeqBatch& sb, int B, int T, int k, int32_t* idx,
+                             int32_t* idx_rows, hipStream_t st) {
+  const int64_t rows = (int64_t)B * T;
+  if (rows < 1 || rows > 0x7FFFFFFF || !sb.len) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, st, scores, ld, sb.max_len, T, k,
+                     idx, sb, idx_rows);
+  return hipGetLastError();
+}
 
 }  // namespace dsa

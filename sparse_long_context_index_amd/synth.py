@@ -53,7 +53,7 @@ PLANT_GAMMA = 8.0
 _SLOTS = {"q_idx": 0, "w": 1, "k_idx": 2, "q": 3, "k": 4, "v": 5, "sink": 6,
           "plant_pos": 7, "plant_tok": 8, "seq_len": 9,
           "ap_idx_q": 10, "ap_idx_k": 11, "ap_q": 12, "ap_k": 13, "ap_v": 14,
-          "ln_gamma": 15, "ln_beta": 16}
+          "ln_gamma": 15, "ln_beta": 16, "batch_len": 17}
 
 _CHUNK = 1 << 22  # elements per generation/encoding chunk
 
@@ -216,6 +216,20 @@ def swa_inputs(cfg: SwaConfig) -> Dict[str, np.ndarray]:
         "sink": normal_f32(_rng(cfg.seed, "sink"), (Q_HEADS,)),
         "sm_scale": np.float32(1.0 / math.sqrt(QK_DIM)),
     }
+
+
+def batch_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Seeded ragged key counts (history plus new tokens) of a decode batch,
+    uniform in [lo, hi]."""
+    return _rng(seed, "batch_len").integers(lo, hi + 1, size=B).astype(np.int64)
+
+
+def batch_inputs(lengths, T: int, k: int, seed: int, plant_frac: float = 0.01) -> list:
+    """Per-sequence decode inputs of a batch: sequence b has lengths[b] keys
+    (its history and its T new tokens), drawn like decode_inputs."""
+    return [decode_inputs(DecodeConfig(f"b{b}", L=int(n) - T, T=T, k=k, plant_frac=plant_frac,
+                                       seed=seed * 1009 + b))
+            for b, n in enumerate(lengths)]
 
 
 def sample_rows(T: int, n: int = 64, seed: int = 4) -> np.ndarray:

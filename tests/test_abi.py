@@ -174,3 +174,28 @@ def test_prefill_topk_validation(L):
     assert call(ws=None) == 5
     assert call(nb=ws_need - 1) == 5
     assert call(ws=MIS) == 4
+
+
+def test_decode_batch_validation(L):
+    f = L.dsa_decode_batch
+    need = L.dsa_workspace_bytes(binding.OP_DECODE_BATCH, 65536, 1, 2048, 64)
+    assert need > 64 * 65536 * 4                          # the scores of the batch
+    assert L.dsa_workspace_bytes(binding.OP_DECODE_BATCH, 65536, 17, 2048, 64) == 0   # T > 16
+    assert L.dsa_workspace_bytes(binding.OP_DECODE_BATCH, 65536, 1, 2048, 0) == 0
+    assert L.dsa_workspace_bytes(binding.OP_DECODE_BATCH, 30000, 1, 100, 8) <= need
+
+    def call(qi=A, w=A, ki=A, q=A, kc=A, vc=A, n_rows=10 ** 6, ss=A, sl=A, B=64, T=1, max_len=65536, k=2048,
+             sink=A, sm=0.07, out=A, lse=None, idx=None, ws=A, nb=need):
+        return f(qi, w, ki, q, kc, vc, n_rows, ss, sl, B, T, max_len, k, sink, sm, out, lse, idx, ws, nb, None)
+    assert call(ss=None) == 1
+    assert call(out=None) == 1
+    assert call(sl=MIS) == 4
+    assert call(idx=MIS) == 4
+    assert call(B=0) == 2
+    assert call(T=17) == 2
+    assert call(max_len=0) == 2
+    assert call(k=0) == 2
+    assert call(n_rows=0) == 2
+    assert call(sm=float("inf")) == 2
+    assert call(ws=None) == 5
+    assert call(nb=need - 1) == 5

@@ -412,3 +412,25 @@ def test_sink_pin_catches_scaled_sink_mutant(monkeypatch):
     monkeypatch.setattr(oracle.dsa_oracle, "attend", mutant)
     with pytest.raises(AssertionError):
         test_attention_full_set_equals_dense_causal(True, 4)
+
+
+# ---------------------------------------------------------------- batched decode
+
+def test_batch_oracle_reduces_to_the_single_step_and_is_order_free():
+    lens = synth.batch_lengths(3, 40, 3000, seed=2)
+    seqs = synth.batch_inputs(lens, T=2, k=64, seed=2)
+    res = oracle.dsa_decode_batch(seqs, 64)
+    for s, r in zip(seqs, res):
+        one = oracle.dsa_decode_step(s, 64)
+        for x, y in zip(r, one):
+            assert np.array_equal(np.asarray(x), np.asarray(y), equal_nan=True)
+    rev = oracle.dsa_decode_batch(seqs[::-1], 64)
+    for x, y in zip(res, rev[::-1]):
+        assert np.array_equal(x[1], y[1])
+        assert np.array_equal(x[2], y[2])
+
+
+def test_batch_lengths_are_seeded_and_in_range():
+    a = synth.batch_lengths(64, 256, 65536, seed=9)
+    assert np.array_equal(a, synth.batch_lengths(64, 256, 65536, seed=9))
+    assert a.min() >= 256 and a.max() <= 65536 and len(set(a.tolist())) > 50
