@@ -258,6 +258,36 @@ def dsa_decode_step(inp: dict, k: int, sink=True):
     return S, idx, out, lse
 
 
+# --------------------------------------------------------------------------
+# Index-selection recall ([NoFA] "How much of this did AI actually build?":
+# the indexer's top-k was checked against a full-attention reference).  The
+# share of each head's dense softmax mass, over every visible key and without
+# the sink, that falls on the selected keys.
+# --------------------------------------------------------------------------
+
+def index_recall(q_bits, k_bits, idx, Lk: int, T: int, sm_scale: float):
+    """recall [T,64] and the dense log-sum-exp lse_dense [T,64] (natural log)
+    of the logits sm_scale * q . k over keys 0 .. p_t."""
+    hkv = k_bits.shape[1]
+    grp = Q_HEADS // hkv
+    rec = np.zeros((T, Q_HEADS))
+    lse = np.zeros((T, Q_HEADS))
+    for t in range(T):
+        n = Lk - T + t + 1
+        Kt = decode_bf16(k_bits[:n])                  # [n,Hkv,192]
+        qt = decode_bf16(q_bits[t])                   # [64,192]
+        sel = np.asarray(idx[t], dtype=np.int64)
+        sel = sel[(sel >= 0) & (sel < n)]
+        for h in range(Q_HEADS):
+            z = sm_scale * (Kt[:, h // grp] @ qt[h])
+            m = z.max()
+            e = np.exp(z - m)
+            tot = e.sum()
+            rec[t, h] = e[sel].sum() / tot
+            lse[t, h] = m + np.log(tot)
+    return rec, lse
+
+
 def dsa_decode_batch(seqs: list, k: int, sink=True):
     """Decode step of several sequences: each is its own DSA decode step over
     its own keys (sharing a cache is storage, not arithmetic), so the batch is

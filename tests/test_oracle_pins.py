@@ -434,3 +434,53 @@ def test_batch_lengths_are_seeded_and_in_range():
     a = synth.batch_lengths(64, 256, 65536, seed=9)
     assert np.array_equal(a, synth.batch_lengths(64, 256, 65536, seed=9))
     assert a.min() >= 256 and a.max() <= 65536 and len(set(a.tolist())) > 50
+
+
+# ---------------------------------------------------------------- index recall
+
+def _recall_inputs(T, Lk, seed):
+    rng = np.random.default_rng(seed)
+    q = synth.encode_bf16((rng.standard_normal((T, 64, 192)) * 2).astype(np.float32))
+    k = synth.encode_bf16(rng.standard_normal((Lk, 4, 192)).astype(np.float32))
+    v = synth.encode_bf16(rng.standard_normal((Lk, 4, 128)).astype(np.float32))
+    return q, k, v
+
+
+def test_recall_of_every_visible_key_is_one_and_of_none_is_zero():
+    T, Lk = 2, 40
+    q, k, _ = _recall_inputs(T, Lk, 1)
+    full = np.stack([np.where(np.arange(64) <= Lk - T + t, np.arange(64), -1) for t in range(T)])
+    rec, _ = oracle.index_recall(q, k, full, Lk, T, 1 / math.sqrt(192))
+    assert np.allclose(rec, 1.0, atol=1e-12)
+    rec0, _ = oracle.index_recall(q, k, -np.ones((T, 8), int), Lk, T, 1 / math.sqrt(192))
+    assert np.all(rec0 == 0)
+
+
+def test_recall_matches_the_attention_log_sum_exps():
+    # recall = exp(lse over the set - lse over every visible key), with the
+    # set's lse from the attention oracle (no sink)
+    T, Lk = 3, 300
+    q, k, v = _recall_inputs(T, Lk, 2)
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.sort(rng.choice(Lk - T + t + 1, 50, replace=False)) for t in range(T)])
+    sm = 1 / math.sqrt(192)
+    rec, lse_dense = oracle.index_recall(q, k, idx, Lk, T, sm)
+    _, lse_sel = oracle.sparse_attention(q, k, v, idx, None, sm)
+    allv = np.stack([np.where(np.arange(Lk) <= Lk - T + t, np.arange(Lk), -1) for t in range(T)])
+    _, lse_all = oracle.sparse_attention(q, k, v, allv, None, sm)
+    assert np.allclose(lse_dense, lse_all, atol=1e-10)
+    assert np.allclose(rec, np.exp(lse_sel - lse_dense), rtol=1e-10)
+
+
+def test_recall_brute_force_tiny_and_monotone():
+    T, Lk = 1, 5
+    q, k, _ = _recall_inputs(T, Lk, 4)
+    sm = 0.3
+    qf, kf = oracle.decode_bf16(q), oracle.decode_bf16(k)
+    sel = [1, 3]
+    rec, _ = oracle.index_recall(q, k, np.array([sel]), Lk, T, sm)
+    for h in (0, 17, 63):
+        e = [math.exp(sm * float(np.dot(qf[0, h], kf[j, h // 16]))) for j in range(Lk)]
+        assert math.isclose(rec[0, h], (e[1] + e[3]) / sum(e), rel_tol=1e-12)
+    rec2, _ = oracle.index_recall(q, k, np.array([[0, 1, 3]]), Lk, T, sm)
+    assert np.all(rec2 >= rec)
