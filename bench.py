@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-batch", action="store_true")
+    ap.add_argument("--no-recall", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run 4 plain device copies of this many bytes (calibrates HBM counters)")
@@ -172,6 +173,8 @@ def main():
         result["cache_append"] = bench_append(torch, binding, dev, inst[0], reps)
     if not args.no_batch:
         result["decode_batch"] = bench_batch(torch, np, binding, synth, dev, reps)
+    if not args.no_recall:
+        result["index_recall"] = bench_recall(torch, binding, dev, inst[0], sm, reps)
     if not args.no_prefill:
         del scores
         result["prefill_indexer"] = bench_prefill(torch, np, binding, synth, dev)
@@ -370,6 +373,27 @@ def bench_batch(torch, np, binding, synth, dev, reps, B=64):
     return {"workload": "dsa_decode_batch b64 lengths U[256,65536] T=1 k=2048", "us": round(us, 3),
             "tokens_per_s": round(B / (us * 1e-6), 1), "bytes": nbytes, "achieved": round(gbs, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+
+
+def bench_recall(torch, binding, dev, x, sm, reps):
+    """dsa_index_recall of the decode step's own top-2,048 at 1M keys: the
+    dense pass reads every visible key's K row of all 4 KV heads."""
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    binding.dsa_decode_step(x["q_idx"], x["w"], x["k_idx"], x["q"], x["k"], x["v"], LK, T, K, x["sink"], sm,
+                            idx_out=idx)
+    ws = binding.Workspace(binding.workspace_bytes(binding.OP_INDEX_RECALL, LK, T, K))
+    rec = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    call = lambda: binding.dsa_index_recall(x["q"], x["k"], x["v"], LK, idx, sm, recall=rec, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [call() for _ in range(4)])
+    us = replay_ms(torch, g, max(reps // 4, 5))[0] / 4 * 1e3
+    nbytes = LK * 4 * 192 * 2 + BYTES_GATHER + T * 64 * 192 * 2 + T * K * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "dsa_index_recall 1M keys, T=1, the decode step's top-2048", "us": round(us, 3),
+            "bytes": nbytes, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "mean_recall": round(float(rec.mean().item()), 6)}
 
 
 def cpu_baseline(d, n_steps):

@@ -95,7 +95,8 @@ typedef enum dsa_op {
   DSA_OP_SWA_ATTN = 3,
   DSA_OP_DECODE_STEP = 4,
   DSA_OP_PREFILL_TOPK = 5,
-  DSA_OP_DECODE_BATCH = 6
+  DSA_OP_DECODE_BATCH = 6,
+  DSA_OP_INDEX_RECALL = 7
 } dsa_op;
 
 /*
@@ -237,6 +238,27 @@ dsa_status dsa_decode_batch(const uint8_t* q_idx, const float* w, const uint8_t*
                             const int64_t* seq_start, const int32_t* seq_len, int32_t B, int32_t T,
                             int64_t max_len, int32_t k, const float* sink, float sm_scale, uint16_t* out,
                             float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_index_recall -- how much of dense attention an index set keeps ([NoFA]
+ * "How much of this did AI actually build?": the indexer's top-k was checked
+ * against a full-attention reference).  For every query token t and head h:
+ *
+ *   recall[t,h] = sum_{j in idx[t]} e^{z_j} / sum_{j <= p_t} e^{z_j},
+ *   z_j = sm_scale * <q[t,h], k_cache[j, h / 16]>   (no sink on either side)
+ *
+ *   q [T][64][192], k_cache [Lk][4][192], v_cache [Lk][4][128] bf16 (v is
+ *   read for the selected rows only); idx [T][k] as dsa_topk writes it;
+ *   recall [T][64] f32; lse_dense [T][64] f32 (optional): log of the
+ *   denominator.  An empty set has recall 0.
+ * The numerator comes from the gathered attention over idx, the denominator
+ * from a QK-only pass over every visible key (Lk * 1.5 KiB of K per token).
+ * Limits: 1 <= T <= min(Lk, 65535), Lk < 2^31, 1 <= k <= 2048.  Needs ws
+ * (DSA_OP_INDEX_RECALL).
+ */
+dsa_status dsa_index_recall(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t Lk,
+                            const int32_t* idx, int32_t T, int32_t k, float sm_scale, float* recall,
+                            float* lse_dense, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dsa_prefill_topk -- dsa_index_scores followed by dsa_topk for many query

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 DSA_OK = 0
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
           4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK, OP_DECODE_BATCH = range(7)
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK, OP_DECODE_BATCH, \
+    OP_INDEX_RECALL = range(8)
 
 IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
 ROPE_BASE = 1.0e7          # DSA_ROPE_BASE
@@ -48,6 +49,7 @@ _SIGS = {
     "dsa_prefill_topk": ([_P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "dsa_decode_batch": ([_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32, _P, _F, _P, _P, _P,
                           _P, _SZ, _P], _I32),
+    "dsa_index_recall": ([_P, _P, _P, _I64, _P, _I32, _I32, _F, _P, _P, _P, _SZ, _P], _I32),
     "dsa_workspace_bytes": ([_I32, _I64, _I32, _I32, _I32], _SZ),
     "dsa_workspace_init": ([_P, _SZ, _P], _I32),
     "dsa_status_string": ([_I32], ctypes.c_char_p),
@@ -162,6 +164,19 @@ def dsa_decode_batch(q_idx, w, k_idx, q, k_cache, v_cache, seq_start, seq_len, m
                                    _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
                                    _dev(idx_out, "idx_out"), ws.ptr, ws.nbytes, _stream()), "dsa_decode_batch")
     return out
+
+
+def dsa_index_recall(q, k_cache, v_cache, Lk: int, idx, sm_scale: float, recall=None, lse_dense=None,
+                     ws: Optional[Workspace] = None):
+    """Share of each head's dense softmax mass on the keys idx [T,k] selects."""
+    T, k = int(idx.shape[0]), int(idx.shape[1])
+    if recall is None:
+        recall = torch.empty((T, Q_HEADS), dtype=torch.float32, device=q.device)
+    ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_INDEX_RECALL, Lk, T, k))
+    _check(load().dsa_index_recall(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk,
+                                   _dev(idx, "idx"), T, k, float(sm_scale), _dev(recall, "recall"),
+                                   _dev(lse_dense, "lse_dense"), ws.ptr, ws.nbytes, _stream()), "dsa_index_recall")
+    return recall
 
 
 def dsa_prefill_topk(q_idx, w, k_idx, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] = None):

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "index_scores.hip", "prefill_scores.hip", "prefill_topk.hip", "topk.hip", "attn.hip", "decode.hip", "append.hip"]
+SOURCES = ["api.hip", "index_scores.hip", "prefill_scores.hip", "prefill_topk.hip", "topk.hip", "attn.hip", "decode.hip", "append.hip", "recall.hip"]
 # per-source extra flags: the prefill contraction keeps its MFMA results in
 # VGPRs, which saves the accumulation-register reads of its epilogue
 EXTRA = {"prefill_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
@@ -46,7 +46,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     objs = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES]
     cmds = [[hipcc, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(9, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)

@@ -138,6 +138,26 @@ BatchLayout batch_layout(int64_t max_len, int T, int k, int B) {
 
 constexpr int kBatchTMax = 16;
 
+// workspace of the recall measurement
+struct RecallLayout {
+  size_t attn, out, lse, part, total;
+};
+
+RecallLayout recall_layout(int64_t Lk, int T, int k) {
+  RecallLayout d;
+  size_t off = kCounterRegionBytes;
+  d.attn = off;
+  off += align_up(attn_scratch_bytes(T, k, DSA_KV_HEADS));
+  d.out = off;
+  off += align_up((size_t)T * DSA_Q_HEADS * DSA_V_DIM * sizeof(uint16_t));
+  d.lse = off;
+  off += align_up((size_t)T * DSA_Q_HEADS * sizeof(float));
+  d.part = off;
+  off += align_up((size_t)T * DSA_KV_HEADS * recall_chunks(Lk) * 32 * sizeof(float));
+  d.total = off;
+  return d;
+}
+
 }  // namespace
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
@@ -191,6 +211,9 @@ size_t dsa_workspace_bytes(dsa_op op, int64_t Lk, int32_t T, int32_t k, int32_t 
           (int64_t)B * T > 0x7FFFFFFF)
         return 0;
       return batch_layout(Lk, T, k, B).total;
+    case DSA_OP_INDEX_RECALL:
+      if (T < 1 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX || T > 65535) return 0;
+      return recall_layout(Lk, T, k).total;
     case DSA_OP_PREFILL_TOPK:
       if (T < 1 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return 0;
       return prefill_layout(Lk, T).total;
@@ -382,6 +405,40 @@ dsa_status dsa_decode_batch(const uint8_t* q_idx, const float* w, const uint8_t*
     a.lse = lse;
     e = launch_sparse_attn(a, base + d.attn, st);
   }
+  return hip_status(e);
+}
+
+dsa_status dsa_index_recall(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int64_t Lk,
+                            const int32_t* idx, int32_t T, int32_t k, float sm_scale, float* recall,
+                            float* lse_dense, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || !recall) return DSA_ERR_NULL;
+  if (!aligned16(idx) || !aligned16(recall) || (lse_dense && !aligned16(lse_dense))) return DSA_ERR_ALIGN;
+  // the output check needs a non-null pointer; the attention output lives in ws
+  dsa_status s = check_attn_args(q, k_cache, v_cache, recall, nullptr, nullptr, sm_scale);
+  if (s != DSA_OK) return s;
+  if (T < 1 || T > 65535 || Lk < T || Lk >= kMaxLk || k < 1 || k > DSA_TOPK_MAX) return DSA_ERR_SHAPE;
+  const RecallLayout d = recall_layout(Lk, T, k);
+  if (!ws || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* lse_sel = reinterpret_cast<float*>(base + d.lse);
+  AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.n_rows = Lk;
+  a.idx = idx;
+  a.k_len = k;
+  a.T = T;
+  a.sink = nullptr;
+  a.sm_scale = sm_scale;
+  a.out = reinterpret_cast<uint16_t*>(base + d.out);
+  a.lse = lse_sel;
+  hipError_t e = launch_sparse_attn(a, base + d.attn, st);
+  if (e == hipSuccess)
+    e = launch_index_recall(q, k_cache, Lk, T, sm_scale, lse_sel, reinterpret_cast<float*>(base + d.part), recall,
+                            lse_dense, st);
   return hip_status(e);
 }
 

@@ -145,6 +145,13 @@ hipError_t launch_prefill_theta(const float* sample, int64_t ld, int64_t Lk, int
 hipError_t launch_prefill_refine(const PrefillCand& pc, int64_t Lk, int T, int k, int32_t* idx, uint32_t* nfail,
                                  uint32_t* failed, hipStream_t st);
 
+// ---- index-selection recall (recall.hip)
+int recall_chunks(int64_t Lk);
+// part: [T][4][recall_chunks(Lk)][32] floats; lse_sel [T][64] from the
+// gathered attention without sink; lse_dense optional
+hipError_t launch_index_recall(const uint16_t* q, const uint16_t* k, int64_t Lk, int T, float sm_scale,
+                               const float* lse_sel, float* part, float* recall, float* lse_dense, hipStream_t st);
+
 // ---- cache append (LayerNorm / partial RoPE / fp8 of the indexer, RoPE of attention q, k)
 hipError_t launch_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
                                const float* ln_beta, float ln_eps, const uint16_t* q, const uint16_t* k,

@@ -199,3 +199,23 @@ def test_decode_batch_validation(L):
     assert call(sm=float("inf")) == 2
     assert call(ws=None) == 5
     assert call(nb=need - 1) == 5
+
+
+def test_index_recall_validation(L):
+    f = L.dsa_index_recall
+    need = L.dsa_workspace_bytes(binding.OP_INDEX_RECALL, 1 << 20, 1, 2048, 0)
+    assert need > 0
+    assert L.dsa_workspace_bytes(binding.OP_INDEX_RECALL, 10, 11, 2048, 0) == 0
+
+    def call(q=A, kc=A, vc=A, Lk=1 << 20, idx=A, T=1, k=2048, sm=0.07, rec=A, lse=None, ws=A, nb=need):
+        return f(q, kc, vc, Lk, idx, T, k, sm, rec, lse, ws, nb, None)
+    assert call(idx=None) == 1
+    assert call(rec=None) == 1
+    assert call(q=None) == 1
+    assert call(rec=MIS) == 4
+    assert call(lse=MIS) == 4
+    assert call(T=0) == 2
+    assert call(k=2049) == 2
+    assert call(Lk=0) == 2
+    assert call(sm=float("nan")) == 2
+    assert call(nb=need - 1) == 5
