@@ -98,10 +98,14 @@ constexpr int kSplitNW = 2;                     // waves per workgroup when a un
 constexpr int kSplitChunk = kSplitNW * kTileKeys;
 
 int sparse_chunks(int T, int k_len) {
-  // split a unit's key list over several workgroups only when the grid is small
-  if (T * DSA_KV_HEADS >= 256) return 1;
-  const int c = (k_len + kSplitChunk - 1) / kSplitChunk;
-  return c < kMaxChunks ? c : kMaxChunks;
+  // split a unit's key list over several workgroups until the grid has about
+  // 1,024 of them (4 per CU), with at least one 64-key tile pair per chunk
+  const int units = T * DSA_KV_HEADS;
+  if (units >= 1024) return 1;
+  int c = (1024 + units - 1) / units;
+  const int by_keys = (k_len + kSplitChunk - 1) / kSplitChunk;
+  c = c < by_keys ? c : by_keys;
+  return c < kMaxChunks ? (c > 1 ? c : 1) : kMaxChunks;
 }
 
 }  // namespace

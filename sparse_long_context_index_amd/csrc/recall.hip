@@ -117,21 +117,33 @@ __global__ __launch_bounds__(256) void dense_lse_kernel(const uint16_t* __restri
   }
 }
 
-// per (t, h): merge the chunks into lse_dense, then recall = exp(lse_sel - lse_dense)
+// per (t, h), one wave: the lanes merge strided chunks, then the wave
+// combines its lanes; lse_dense, then recall = exp(lse_sel - lse_dense)
 __global__ __launch_bounds__(64) void recall_merge_kernel(const float* __restrict__ part, int n_chunks,
                                                           const float* __restrict__ lse_sel, float* __restrict__ recall,
                                                           float* __restrict__ lse_dense) {
-  const int t = blockIdx.x, h = threadIdx.x;
+  const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int g = h / 16, hh = h % 16;
-  const float* pp = part + ((size_t)t * DSA_KV_HEADS + g) * n_chunks * 32;
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, pp[(size_t)c * 32 + 2 * hh]);
-  float L = 0.f;
-  if (M != -INFINITY)
-    for (int c = 0; c < n_chunks; ++c) {
-      const float mc = pp[(size_t)c * 32 + 2 * hh];
-      if (mc != -INFINITY) L += pp[(size_t)c * 32 + 2 * hh + 1] * exp2f(mc - M);
+  const float* pp = part + ((size_t)t * DSA_KV_HEADS + g) * n_chunks * 32 + 2 * hh;
+  float M = -INFINITY, L = 0.f;
+  for (int c = lane; c < n_chunks; c += 64) {
+    const float mc = pp[(size_t)c * 32], lc = pp[(size_t)c * 32 + 1];
+    const float mn = fmaxf(M, mc);
+    if (mn != -INFINITY) {
+      L = L * exp2f(M - mn) + lc * exp2f(mc - mn);
+      M = mn;
     }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(M, o, 64), lo = __shfl_xor(L, o, 64);
+    const float mn = fmaxf(M, mo);
+    if (mn != -INFINITY) {
+      L = L * exp2f(M - mn) + lo * exp2f(mo - mn);
+      M = mn;
+    }
+  }
+  if (lane != 0) return;
   const float ld = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
   const float ls = lse_sel[(size_t)t * DSA_Q_HEADS + h];
   recall[(size_t)t * DSA_Q_HEADS + h] = (ls == -INFINITY || ld == -INFINITY) ? 0.f : expf(ls - ld);
@@ -148,8 +160,8 @@ hipError_t launch_index_recall(const uint16_t* q, const uint16_t* k, int64_t Lk,
   hipLaunchKernelGGL(dense_lse_kernel, dim3(nc, DSA_KV_HEADS, T), dim3(256), 0, st, q, k, Lk, T, sm_scale, nc, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(recall_merge_kernel, dim3(T), dim3(64), 0, st, (const float*)part, nc, lse_sel, recall,
-                     lse_dense);
+  hipLaunchKernelGGL(recall_merge_kernel, dim3(T, DSA_Q_HEADS), dim3(64), 0, st, (const float*)part, nc, lse_sel,
+                     recall, lse_dense);
   return hipGetLastError();
 }
 
