@@ -384,7 +384,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   if (!all_mode) {
     for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;
     __syncthreads();
-    for (int64_t s = threadIdx.x; s < n; s += kRowThreads) atomicAdd(&hist[order_key(row[s]) >> 20], 1u);
+    // 32 independent loads in flight per thread
+    constexpr int kH = 32;
+    for (int64_t s0 = threadIdx.x; s0 < n; s0 += kH * kRowThreads) {
+      float v[kH];
+#pragma unroll
+      for (int e = 0; e < kH; ++e) {
+        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        v[e] = row[s < n ? s : n - 1];
+      }
+#pragma unroll
+      for (int e = 0; e < kH; ++e)
+        if (s0 + (int64_t)e * kRowThreads < n) atomicAdd(&hist[order_key(v[e]) >> 20], 1u);
+    }
     __syncthreads();
     find_threshold_bin<kRowThreads, kHistBins>(hist, (uint32_t)k, fs.scan, &s_b1, &s_above1);
     b1 = s_b1;
@@ -392,31 +404,51 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;   // becomes h2
     __syncthreads();
   }
-  // ordered compaction of candidates (level-1 digit >= b1) into LDS; four
-  // consecutive elements per thread per round
+  // ordered compaction of candidates (level-1 digit >= b1) into LDS.  A
+  // round covers kPer * kRowThreads elements, element base + e * kRowThreads
+  // + tid in thread tid (coalesced loads, all issued first); positions follow
+  // the index order (e, wave, lane): per-(e, wave) counts from the ballots,
+  // one scan over them, then each lane's rank in its ballot.
+  constexpr int kPer = 24;
+  constexpr int kW = kRowThreads / 64;
+  __shared__ uint32_t woff[kPer * kW];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
   uint32_t count = 0;
-  for (int64_t base = 0; base < n; base += 4 * kRowThreads) {
-    const int64_t s0 = base + 4 * (int64_t)threadIdx.x;
-    uint32_t key[4];
-    uint32_t c = 0;
+  for (int64_t base = 0; base < n; base += (int64_t)kPer * kRowThreads) {
+    uint32_t key[kPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[e] = (s0 + e < n) ? order_key(row[s0 + e]) : 0u;
-      const bool f = (s0 + e < n) && (key[e] >> 20) >= b1;
-      c += f;
-      if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&hist[(key[e] >> 8) & 0xFFF], 1u);
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
+      key[e] = __float_as_uint(row[s < n ? s : n - 1]);
     }
-    uint32_t tot;
-    uint32_t p = count + block_excl_scan<kRowThreads>(c, fs.scan, &tot);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool f = (s0 + e < n) && (key[e] >> 20) >= b1;
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
+      key[e] = s < n ? order_key(__uint_as_float(key[e])) : 0u;
+      const bool f = s < n && (key[e] >> 20) >= b1;
+      if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&hist[(key[e] >> 8) & 0xFFF], 1u);
+      const uint64_t m = __ballot(f);
+      if (lane == e) woff[e * kW + wv] = (uint32_t)__builtin_popcountll(m);
+    }
+    __syncthreads();
+    uint32_t tot;
+    const uint32_t x = threadIdx.x < kPer * kW ? woff[threadIdx.x] : 0u;
+    const uint32_t off = block_excl_scan<kRowThreads>(x, fs.scan, &tot);
+    if (threadIdx.x < kPer * kW) woff[threadIdx.x] = off;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
+      const bool f = s < n && (key[e] >> 20) >= b1;
+      const uint64_t m = __ballot(f);
       if (f) {
-        if (p < kRowCap) cand[p] = make_uint2(key[e], (uint32_t)(s0 + e));
-        ++p;
+        const uint32_t p = count + woff[e * kW + wv] + (uint32_t)__builtin_popcountll(m & below);
+        if (p < kRowCap) cand[p] = make_uint2(key[e], (uint32_t)s);
       }
     }
     count += tot;
+    __syncthreads();                                   // woff is rewritten by the next round
   }
   __syncthreads();
   if (count <= kRowCap) {
