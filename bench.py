@@ -65,6 +65,7 @@ def parse():
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-batch", action="store_true")
     ap.add_argument("--no-recall", action="store_true")
+    ap.add_argument("--no-swa", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run 4 plain device copies of this many bytes (calibrates HBM counters)")
@@ -175,6 +176,8 @@ def main():
         result["decode_batch"] = bench_batch(torch, np, binding, synth, dev, reps)
     if not args.no_recall:
         result["index_recall"] = bench_recall(torch, binding, dev, inst[0], sm, reps)
+    if not args.no_swa:
+        result["swa_decode"] = bench_swa(torch, np, binding, synth, dev, reps)
     if not args.no_prefill:
         del scores
         result["prefill_indexer"] = bench_prefill(torch, np, binding, synth, dev)
@@ -394,6 +397,39 @@ def bench_recall(torch, binding, dev, x, sm, reps):
             "bytes": nbytes, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
             "mean_recall": round(float(rec.mean().item()), 6)}
+
+
+def bench_swa(torch, np, binding, synth, dev, reps):
+    """swa_attn on the swa_decode_b64 workload: 64 sequences with lengths
+    uniform in [256, 65536], one query token each, window 128, 8 KV heads;
+    full-length ragged caches drawn on the device (only the windows are read).
+    Algorithmic bytes: each sequence's window of K and V rows for 8 KV heads
+    plus its query and output."""
+    cfg = synth.CONFIGS["swa_decode_b64"]
+    lens = synth._rng(cfg.seed, "seq_len").integers(cfg.len_lo, cfg.len_hi + 1, size=cfg.B).astype(np.int64)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    n_rows = int(lens.sum())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(51)
+    bf = lambda *sh: torch.randn(sh, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    Kc, Vc = bf(n_rows, 8, 192), bf(n_rows, 8, 128)
+    q = bf(cfg.B, 64, 192)
+    sink = torch.randn((64,), generator=gen, device=dev)
+    st = torch.from_numpy(starts).to(dev)
+    sl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    ws = binding.Workspace(binding.workspace_bytes(binding.OP_SWA_ATTN, B=cfg.B))
+    out = torch.empty((cfg.B, 64, 128), dtype=torch.bfloat16, device=dev)
+    call = lambda: binding.swa_attn(q, Kc, Vc, st, sl, cfg.window, sink, 1.0 / 192 ** 0.5, out=out, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [call() for _ in range(8)])
+    us = replay_ms(torch, g, max(reps // 8, 10))[0] / 8 * 1e3
+    nbytes = int(np.minimum(lens, cfg.window).sum()) * 8 * 320 * 2 + cfg.B * (64 * 192 * 2 + 64 * 128 * 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del Kc, Vc
+    return {"workload": "swa_decode_b64 (64 sequences, window 128, GQA8)", "us": round(us, 3), "bytes": nbytes,
+            "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bound": "hbm (latency at this size)"}
 
 
 def cpu_baseline(d, n_steps):
