@@ -112,7 +112,7 @@ def check_append(out, inp, Lk, T, ln=True):
 
 
 @pytest.mark.parametrize("T,Lk", [(1, 1), (1, 8192), (4, 131072), (3, 1000), (8, 1048576), (1, 1048576),
-                                  (64, 70000)])
+                                  (64, 70000), (511, 4000), (512, 512), (600, 2000), (1100, 70000)])
 def test_cache_append(dev, T, Lk):
     inp = synth.append_inputs(T, seed=T * 7 + Lk % 1000)
     out = run_append(dev, inp, Lk, T)
@@ -125,13 +125,14 @@ def test_cache_append_without_layer_norm_gain_and_bias(dev):
     check_append(out, inp, 4096, 5, ln=False)
 
 
-def test_cache_append_extreme_values(dev):
+@pytest.mark.parametrize("T", [4, 520])
+def test_cache_append_extreme_values(dev, T):
     # large activations saturate the fp8 codes at +-448; tiny ones land in the
     # e4m3 subnormal range; a constant index key normalises to the bias alone
-    T, Lk = 4, 5000
+    Lk = 5000
     inp = synth.append_inputs(T, seed=9)
     rng = np.random.default_rng(9)
-    big = (rng.standard_normal((T, 16, 128)) * np.array([1e3, 1e-3, 1.0, 3e2])[:, None, None]).astype(np.float32)
+    big = (rng.standard_normal((T, 16, 128)) * np.resize([1e3, 1e-3, 1.0, 3e2], T)[:, None, None]).astype(np.float32)
     inp["idx_q"] = synth.encode_bf16(big)
     inp["idx_k"] = inp["idx_k"].copy()
     inp["idx_k"][1] = inp["idx_k"][1, 0]
