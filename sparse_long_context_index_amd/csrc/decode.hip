@@ -102,7 +102,11 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
   // is in flight at once
   const uint32_t* key_row = d.lkeys + (size_t)t * kListM * nl;
   const uint32_t* idx_row = d.lidx + (size_t)t * kListM * nl;
-  uint32_t kA[kLPT][kListM], iA[kLPT][kListM], n[kLPT];
+  // cth = ceil(k / lists): the cth-th entry of every list bounds the threshold
+  // from below (loaded with the lists, see step 2)
+  const uint32_t cth = (uint32_t)((k + nl - 1) / nl);
+  const int cj = cth < (uint32_t)kListM ? (int)cth - 1 : kListM - 1;
+  uint32_t kA[kLPT][kListM], iA[kLPT][kListM], n[kLPT], kc[kLPT];
   bool full[kLPT];
 #pragma unroll
   for (int q = 0; q < kLPT; ++q) {
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       kA[q][j] = key_row[j * nl + l];
       iA[q][j] = idx_row[j * nl + l];
     }
+    kc[q] = key_row[cj * nl + l];
     n[q] = lq < nl ? w & 0x7FFFFFFFu : 0u;
     full[q] = lq < nl && (w >> 31) != 0u;
   }
@@ -144,21 +149,32 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     // those lists hold k entries or more that entry bounds the threshold;
     // otherwise the smallest entry of all does.  Spreading the candidates
     // over the bins of this range keeps the LDS atomics apart.
+    // Every pass below visits a list's entries only while they can matter:
+    // the lists are sorted, so the entries at or above a bound form a prefix,
+    // and a wave skips each block of 8 entries that starts past the longest
+    // such prefix among its lanes (the gate `go`, wave-uniform).
     RadixShared& rs = sh.s.rs;
-    const uint32_t cth = (uint32_t)((k + nl - 1) / nl);
     uint32_t kmax = 0u, xc = 0xFFFFFFFFu, xl = 0xFFFFFFFFu, nc = 0u;
 #pragma unroll
     for (int q = 0; q < kLPT; ++q) {
       if (n[q]) kmax = kmax > kA[q][0] ? kmax : kA[q][0];
-      nc += n[q] >= cth;
-#pragma unroll
-      for (int j = 0; j < kListM; ++j) {
-        if ((uint32_t)j + 1 == cth && n[q] >= cth) xc = xc < kA[q][j] ? xc : kA[q][j];
-        if ((uint32_t)j + 1 == n[q]) xl = xl < kA[q][j] ? xl : kA[q][j];
+      if (n[q] >= cth) {
+        ++nc;
+        xc = xc < kc[q] ? xc : kc[q];
       }
     }
     block_reduce_mmms<kDecNT>(kmax, xc, xl, nc, sh.scan);
-    const uint32_t L0 = (uint64_t)nc * cth >= (uint64_t)k ? xc : xl;
+    uint32_t L0 = xc;
+    if ((uint64_t)nc * cth < (uint64_t)k) {    // block-uniform: the smallest entry of all bounds instead
+      uint32_t z0 = 0u, z1 = 0xFFFFFFFFu, z2 = 0u;
+#pragma unroll
+      for (int q = 0; q < kLPT; ++q)
+#pragma unroll
+        for (int j = 0; j < kListM; ++j)
+          if ((uint32_t)j + 1 == n[q]) xl = xl < kA[q][j] ? xl : kA[q][j];
+      block_reduce_mmms<kDecNT>(z0, z1, xl, z2, sh.scan);
+      L0 = xl;
+    }
     const uint32_t span = kmax - L0;
     const int bits = span ? 32 - __builtin_clz(span) : 0;
     const int s1 = bits > 12 ? bits - 12 : 0;   // bits of u = key - L0 below the first digit
@@ -170,10 +186,16 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 #pragma unroll
       for (int q = 0; q < kLPT; ++q)
 #pragma unroll
-        for (int j = 0; j < kListM; ++j) {
-          const uint32_t u = kA[q][j] - L0;
-          if ((uint32_t)j < n[q] && kA[q][j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
-            atomicAdd(&rs.hist[(u >> shift) & mask], 1u);
+        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= L0) != 0ull;
+          if (go) {
+#pragma unroll
+            for (int j = j0; j < j0 + 8; ++j) {
+              const uint32_t u = kA[q][j] - L0;
+              if ((uint32_t)j < n[q] && kA[q][j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
+                atomicAdd(&rs.hist[(u >> shift) & mask], 1u);
+            }
+          }
         }
       __syncthreads();
     };
@@ -183,8 +205,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 #pragma unroll
     for (int q = 0; q < kLPT; ++q)
 #pragma unroll
-      for (int j = 0; j < kListM; ++j)
-        if ((uint32_t)j < n[q] && kA[q][j] >= L0) atomicAdd(&rs.hist[(kA[q][j] - L0) >> s1], 1u);
+      for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+        go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= L0) != 0ull;
+        if (go) {
+#pragma unroll
+          for (int j = j0; j < j0 + 8; ++j)
+            if ((uint32_t)j < n[q] && kA[q][j] >= L0) atomicAdd(&rs.hist[(kA[q][j] - L0) >> s1], 1u);
+        }
+      }
     __syncthreads();
     find_threshold_bin<kDecNT, kHistBins>(rs.hist, (uint32_t)k, rs.scan, &rs.bin, &rs.above);
     const uint32_t b1 = rs.bin;
@@ -208,9 +236,16 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       for (int q = 0; q < kLPT; ++q) {
         ndq[q] = 0;
 #pragma unroll
-        for (int j = 0; j < kListM; ++j) {
-          ndq[q] += (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] > hi);
-          nb += in_b1(q, j);
+        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= lo) != 0ull;
+          if (go) {
+#pragma unroll
+            for (int j = j0; j < j0 + 8; ++j) {
+              const bool in = (uint32_t)j < n[q] && kA[q][j] >= lo;
+              ndq[q] += (uint32_t)(in && kA[q][j] > hi);
+              nb += (uint32_t)(in && kA[q][j] <= hi);
+            }
+          }
         }
         nd += ndq[q];
       }
@@ -221,13 +256,19 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 #pragma unroll
       for (int q = 0; q < kLPT; ++q)
 #pragma unroll
-        for (int j = 0; j < kListM; ++j)
-          if (in_b1(q, j)) {
-            sh.s.ck[pb] = kA[q][j];
-            sh.s.ci[pb] = iA[q][j];
-            if (full[q] && (uint32_t)j + 1 == n[q]) last_slot = (int)pb;
-            ++pb;
+        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= lo) != 0ull;
+          if (go) {
+#pragma unroll
+            for (int j = j0; j < j0 + 8; ++j)
+              if (in_b1(q, j)) {
+                sh.s.ck[pb] = kA[q][j];
+                sh.s.ci[pb] = iA[q][j];
+                if (full[q] && (uint32_t)j + 1 == n[q]) last_slot = (int)pb;
+                ++pb;
+              }
           }
+        }
       const uint32_t ncp = (cnt1 + 15u) & ~15u;  // padded with key 0, which ranks below every entry
       if ((uint32_t)tid >= cnt1 && (uint32_t)tid < ncp) {
         sh.s.ck[tid] = 0u;
@@ -266,8 +307,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 #pragma unroll
         for (int q = 0; q < kLPT; ++q) {
 #pragma unroll
-          for (int j = 0; j < kListM; ++j)      // the entries above the bin lead the list
-            if ((uint32_t)j < ndq[q] && pd + j < (uint32_t)DSA_TOPK_MAX) sh.sel[pd + j] = (int32_t)iA[q][j];
+          for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {   // the entries above the bin lead the list
+            go = go && __ballot((uint32_t)j0 < ndq[q]) != 0ull;
+            if (go) {
+#pragma unroll
+              for (int j = j0; j < j0 + 8; ++j)
+                if ((uint32_t)j < ndq[q] && pd + j < (uint32_t)DSA_TOPK_MAX) sh.sel[pd + j] = (int32_t)iA[q][j];
+            }
+          }
           pd += ndq[q];
         }
         if ((uint32_t)tid < cnt1 && sh.s.rk[tid] < need && above1 + sh.s.rk[tid] < (uint32_t)DSA_TOPK_MAX)
@@ -319,9 +366,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
           cnt[q] = n[q];
         } else {
 #pragma unroll
-          for (int j = 0; j < kListM; ++j)
-            cnt[q] += (uint32_t)((uint32_t)j < n[q]) &
-                      ((uint32_t)(kA[q][j] > tk) | ((uint32_t)(kA[q][j] == tk) & (uint32_t)(iA[q][j] <= ti)));
+          for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+            go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= tk) != 0ull;
+            if (go) {
+#pragma unroll
+              for (int j = j0; j < j0 + 8; ++j)
+                cnt[q] += (uint32_t)((uint32_t)j < n[q] && kA[q][j] >= tk && (kA[q][j] > tk || iA[q][j] <= ti));
+            }
+          }
         }
         hides |= full[q] && cnt[q] == n[q];
       }
@@ -337,8 +389,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
 #pragma unroll
       for (int q = 0; q < kLPT; ++q) {
 #pragma unroll
-        for (int j = 0; j < kListM; ++j)
-          if ((uint32_t)j < cnt[q] && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[q][j];
+        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+          go = go && __ballot((uint32_t)j0 < cnt[q]) != 0ull;
+          if (go) {
+#pragma unroll
+            for (int j = j0; j < j0 + 8; ++j)
+              if ((uint32_t)j < cnt[q] && base + j < (uint32_t)DSA_TOPK_MAX) sh.sel[base + j] = (int32_t)iA[q][j];
+          }
+        }
         base += cnt[q];
       }
       if (n_sel > (uint32_t)DSA_TOPK_MAX) n_sel = DSA_TOPK_MAX;
