@@ -57,7 +57,40 @@ struct DecodeShared {
   };
   int32_t sel[DSA_TOPK_MAX];
   uint32_t scan[32];
+  // written once per launch (no barrier needed before their reuse)
+  uint32_t red[kDecNT / 64][5];                    // step 1's reduction
+  uint32_t bscan[kDecNT / 64], bout[3];            // the first digit's threshold bin
+  uint32_t pscan[kDecNT / 64];                     // the direct path's packed prefix sum
+  alignas(16) uint32_t cf[kC1Cap];                 // threshold-bin entry is a capped list's last
 };
+
+// Block-wide reduction of step 1 with one barrier: sum of n, or of f, max of
+// a, min of b, sum of c.
+__device__ __forceinline__ void reduce_lists(uint32_t& n, uint32_t& f, uint32_t& a, uint32_t& b, uint32_t& c,
+                                             uint32_t (*red)[5]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t rn = wave_incl_scan(n), rc = wave_incl_scan(c);
+  const uint32_t ra = wave_incl_minmax<true>(a), rb = wave_incl_minmax<false>(b);
+  const uint32_t rf = __ballot(f != 0u) != 0ull;
+  if (lane == 63) {
+    red[wv][0] = rn;
+    red[wv][1] = rf;
+    red[wv][2] = ra;
+    red[wv][3] = rb;
+    red[wv][4] = rc;
+  }
+  __syncthreads();
+  n = f = a = c = 0u;
+  b = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kDecNT / 64; ++w) {
+    n += red[w][0];
+    f |= red[w][1];
+    a = a > red[w][2] ? a : red[w][2];
+    b = b < red[w][3] ? b : red[w][3];
+    c += red[w][4];
+  }
+}
 
 struct LdsList {
   const int32_t* sel;
@@ -122,16 +155,23 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     n[q] = lq < nl ? w & 0x7FFFFFFFu : 0u;
     full[q] = lq < nl && (w >> 31) != 0u;
   }
-  uint32_t M;
-  uint32_t n_all = 0;
-  bool full_any = false;
+  // the block's entries M, whether any list is capped, the largest key
+  // kmax, the smallest cth-th entry xc and the lists nc holding cth entries;
+  // meanwhile the first digit's histogram is cleared
+  uint32_t M = 0u, full_any = 0u, kmax = 0u, xc = 0xFFFFFFFFu, nc = 0u;
 #pragma unroll
   for (int q = 0; q < kLPT; ++q) {
-    n_all += n[q];
-    full_any |= full[q];
+    M += n[q];
+    full_any |= (uint32_t)full[q];
+    if (n[q]) kmax = kmax > kA[q][0] ? kmax : kA[q][0];
+    if (n[q] >= cth) {
+      ++nc;
+      xc = xc < kc[q] ? xc : kc[q];
+    }
   }
-  block_excl_scan<kDecNT>(n_all, sh.scan, &M);
-  const bool any_full = __syncthreads_or(full_any);
+  for (int i = tid; i < kHistBins; i += kDecNT) sh.s.rs.hist[i] = 0;
+  reduce_lists(M, full_any, kmax, xc, nc, sh.red);
+  const bool any_full = full_any != 0u;
 
   // ---- 2. the k-th entry (tk, ti) of the union: keep key > tk, or key == tk and index <= ti
   bool fallback;
@@ -154,19 +194,9 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     // and a wave skips each block of 8 entries that starts past the longest
     // such prefix among its lanes (the gate `go`, wave-uniform).
     RadixShared& rs = sh.s.rs;
-    uint32_t kmax = 0u, xc = 0xFFFFFFFFu, xl = 0xFFFFFFFFu, nc = 0u;
-#pragma unroll
-    for (int q = 0; q < kLPT; ++q) {
-      if (n[q]) kmax = kmax > kA[q][0] ? kmax : kA[q][0];
-      if (n[q] >= cth) {
-        ++nc;
-        xc = xc < kc[q] ? xc : kc[q];
-      }
-    }
-    block_reduce_mmms<kDecNT>(kmax, xc, xl, nc, sh.scan);
     uint32_t L0 = xc;
     if ((uint64_t)nc * cth < (uint64_t)k) {    // block-uniform: the smallest entry of all bounds instead
-      uint32_t z0 = 0u, z1 = 0xFFFFFFFFu, z2 = 0u;
+      uint32_t z0 = 0u, z1 = 0xFFFFFFFFu, z2 = 0u, xl = 0xFFFFFFFFu;
 #pragma unroll
       for (int q = 0; q < kLPT; ++q)
 #pragma unroll
@@ -199,9 +229,7 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
         }
       __syncthreads();
     };
-    // first digit: (key - L0) >> s1 over every entry >= L0
-    for (int i = tid; i < kHistBins; i += kDecNT) rs.hist[i] = 0;
-    __syncthreads();
+    // first digit: (key - L0) >> s1 over every entry >= L0 (cleared in step 1)
 #pragma unroll
     for (int q = 0; q < kLPT; ++q)
 #pragma unroll
@@ -214,12 +242,9 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
         }
       }
     __syncthreads();
-    find_threshold_bin<kDecNT, kHistBins>(rs.hist, (uint32_t)k, rs.scan, &rs.bin, &rs.above);
-    const uint32_t b1 = rs.bin;
-    const uint32_t above1 = rs.above;          // entries in the bins above b1
+    uint32_t b1, above1, cnt1;                 // the bin, the entries in the bins above it, in it
+    find_threshold_bin_once<kDecNT, kHistBins>(rs.hist, (uint32_t)k, sh.bscan, sh.bout, &b1, &above1, &cnt1);
     uint32_t need = (uint32_t)k - above1;      // entries still to take from bin b1
-    const uint32_t cnt1 = rs.hist[b1];
-    __syncthreads();
     const uint32_t lo = L0 + (b1 << s1);       // bin b1 holds the keys lo .. hi
     const uint32_t wid = (1u << s1) - 1u;
     const uint32_t hi = lo > 0xFFFFFFFFu - wid ? 0xFFFFFFFFu : lo + wid;
@@ -231,7 +256,10 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       // list) are kept, and the bin's entries are ranked directly -- those of
       // rank < need are kept too.  One packed prefix sum places both groups:
       // [entries above the bin, in list order] then [kept bin entries by rank].
+      // A capped list that keeps its last entry may hide winners: then the
+      // whole selection falls back (step 3).
       uint32_t ndq[kLPT], nd = 0, nb = 0;
+      bool hides = false;
 #pragma unroll
       for (int q = 0; q < kLPT; ++q) {
         ndq[q] = 0;
@@ -248,27 +276,31 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
           }
         }
         nd += ndq[q];
+        hides |= full[q] && n[q] == (uint32_t)kListM && kA[q][kListM - 1] > hi;
       }
       uint32_t tot;
-      const uint32_t packed = block_excl_scan<kDecNT>((nd << 16) | nb, sh.scan, &tot);
-      uint32_t pb = packed & 0xFFFFu;
-      int last_slot = -1;                      // bin slot of this thread's capped list's last entry
+      const uint32_t packed = block_excl_scan_once<kDecNT>((nd << 16) | nb, sh.pscan, &tot);
+      uint32_t pd = packed >> 16, pb = packed & 0xFFFFu;
 #pragma unroll
-      for (int q = 0; q < kLPT; ++q)
+      for (int q = 0; q < kLPT; ++q) {
 #pragma unroll
-        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
+        for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {   // the entries above the bin lead the list
           go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= lo) != 0ull;
           if (go) {
 #pragma unroll
-            for (int j = j0; j < j0 + 8; ++j)
+            for (int j = j0; j < j0 + 8; ++j) {
+              if ((uint32_t)j < ndq[q] && pd + j < (uint32_t)DSA_TOPK_MAX) sh.sel[pd + j] = (int32_t)iA[q][j];
               if (in_b1(q, j)) {
                 sh.s.ck[pb] = kA[q][j];
                 sh.s.ci[pb] = iA[q][j];
-                if (full[q] && (uint32_t)j + 1 == n[q]) last_slot = (int)pb;
+                sh.cf[pb] = (uint32_t)(full[q] && (uint32_t)j + 1 == n[q]);
                 ++pb;
               }
+            }
           }
         }
+        pd += ndq[q];
+      }
       const uint32_t ncp = (cnt1 + 15u) & ~15u;  // padded with key 0, which ranks below every entry
       if ((uint32_t)tid >= cnt1 && (uint32_t)tid < ncp) {
         sh.s.ck[tid] = 0u;
@@ -293,32 +325,13 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
             rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
                     before(k4[q].w, i4[q].w);
         }
-        sh.s.rk[tid] = rank;
+        if (rank < need) {
+          if (above1 + rank < (uint32_t)DSA_TOPK_MAX) sh.sel[above1 + rank] = (int32_t)id;
+          hides |= sh.cf[tid] != 0u;
+        }
       }
-      __syncthreads();
-      // a capped list that keeps its last entry may hide winners
-      bool hides = false;
-#pragma unroll
-      for (int q = 0; q < kLPT; ++q) hides |= full[q] && n[q] == (uint32_t)kListM && kA[q][kListM - 1] > hi;
-      if (last_slot >= 0) hides |= sh.s.rk[last_slot] < need;
       fallback = __syncthreads_or(hides);
       if (!fallback) {
-        uint32_t pd = packed >> 16;
-#pragma unroll
-        for (int q = 0; q < kLPT; ++q) {
-#pragma unroll
-          for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {   // the entries above the bin lead the list
-            go = go && __ballot((uint32_t)j0 < ndq[q]) != 0ull;
-            if (go) {
-#pragma unroll
-              for (int j = j0; j < j0 + 8; ++j)
-                if ((uint32_t)j < ndq[q] && pd + j < (uint32_t)DSA_TOPK_MAX) sh.sel[pd + j] = (int32_t)iA[q][j];
-            }
-          }
-          pd += ndq[q];
-        }
-        if ((uint32_t)tid < cnt1 && sh.s.rk[tid] < need && above1 + sh.s.rk[tid] < (uint32_t)DSA_TOPK_MAX)
-          sh.sel[above1 + sh.s.rk[tid]] = (int32_t)sh.s.ci[tid];
         n_sel_direct = (uint32_t)k;
         direct = true;
       }
@@ -408,8 +421,9 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       n_sel = ordered_keep<kDecNT>(row_key, (int)n_vis, tau, r, sh.scan,
                                    [&](uint32_t pos, int i) { sh.sel[pos] = i; });
     }
+    __syncthreads();
   }
-  __syncthreads();
+  // (on the direct path the fallback vote was the barrier after the last write of sel)
 
   // ---- optional idx output, ascending, written by one workgroup per row
   if (d.idx_out && c == 0 && g == 0) {
@@ -418,8 +432,8 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     bitonic_sort_2048<kDecNT>(sh.sorted);
     int32_t* o = d.idx_out + (size_t)t * k;
     for (int i = tid; i < k; i += kDecNT) o[i] = (uint32_t)i < n_sel ? sh.sorted[i] : -1;
+    __syncthreads();                           // sorted shares its memory with the attention's
   }
-  __syncthreads();
 
   // ---- 4. attention over this workgroup's chunk of the kept list
   const int p0 = c * kDecChunk < (int)n_sel ? c * kDecChunk : (int)n_sel;

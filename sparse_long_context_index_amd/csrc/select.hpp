@@ -136,6 +136,69 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
   __syncthreads();
 }
 
+// block_excl_scan with one barrier: sm (NT / 64 words) is written once and
+// must not be written again by the block without a barrier in between.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_once(uint32_t v, uint32_t* sm, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) sm[wv] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t s = sm[i];
+    base += (i < wv) ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+// find_threshold_bin with two barriers, returning to every thread the bin,
+// the entries in the bins above it and the entries in it.  sm (NT / 64 words)
+// and out (3 words) are written once, as in block_excl_scan_once.
+template <int NT, int NB>
+__device__ __forceinline__ void find_threshold_bin_once(const uint32_t* hist, uint32_t need, uint32_t* sm,
+                                                        uint32_t* out, uint32_t* bin, uint32_t* above,
+                                                        uint32_t* count) {
+  constexpr int PER = NB / NT;
+  static_assert(PER * NT == NB && PER % 4 == 0, "bins per thread");
+  const int base = NB - ((int)threadIdx.x + 1) * PER;      // thread 0 owns the top bins
+  uint32_t h[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(hist + base + i);
+    h[i] = q.x;
+    h[i + 1] = q.y;
+    h[i + 2] = q.z;
+    h[i + 3] = q.w;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += h[i];
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan_once<NT>(sum, sm, &tot);
+  if (excl < need && excl + sum >= need) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (acc + h[i] >= need) {
+        out[0] = (uint32_t)(base + i);
+        out[1] = acc;
+        out[2] = h[i];
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  __syncthreads();
+  *bin = out[0];
+  *above = out[1];
+  *count = out[2];
+}
+
 struct alignas(16) RadixShared {
   uint32_t hist[kHistBins];
   uint32_t scan[16];
