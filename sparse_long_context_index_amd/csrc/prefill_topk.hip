@@ -77,43 +77,8 @@ __global__ __launch_bounds__(kPtNT) void prefill_refine_kernel(PrefillCand pc, i
     ckey[i] = e.x;
     cidx[i] = e.y;
   }
-  if (threadIdx.x == 0) sh.nsel = 0;
   __syncthreads();
-  // threshold key tau and the number r of tau-equal entries kept
-  uint32_t tau, r, eq;
-  radix_threshold<kPtNT>([&](int i) { return ckey[i]; }, (int)n, need, sh.rs, &tau, &r, &eq);
-  // among tau-equal entries the r lowest indices win: threshold on ~index
-  uint32_t imax = 0xFFFFFFFFu;
-  if (eq > r) {
-    uint32_t tau2, r2, eq2;
-    radix_threshold<kPtNT>([&](int i) { return ckey[i] == tau ? ~cidx[i] : 0u; }, (int)n, r, sh.rs, &tau2, &r2,
-                           &eq2);
-    imax = ~tau2;
-  }
-  for (uint32_t i = threadIdx.x; i < n; i += kPtNT) {
-    const uint32_t key = ckey[i], id = cidx[i];
-    if (key > tau || (key == tau && id <= imax)) sh.sel[atomicAdd(&sh.nsel, 1u)] = id;
-  }
-  __syncthreads();
-  for (uint32_t i = need + threadIdx.x; i < (uint32_t)kSortN; i += kPtNT) sh.sel[i] = 0xFFFFFFFFu;
-  // bitonic sort of the kSortN slots, ascending
-  for (int size = 2; size <= kSortN; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int i = threadIdx.x; i < kSortN / 2; i += kPtNT) {
-        const int a = 2 * i - (i & (stride - 1));
-        const int b = a + stride;
-        const uint32_t x = sh.sel[a], y = sh.sel[b];
-        const bool up = (a & size) == 0;
-        if ((x > y) == up) {
-          sh.sel[a] = y;
-          sh.sel[b] = x;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < k; j += kPtNT) out[j] = j < (int)need ? (int32_t)sh.sel[j] : -1;
+  select_sorted<kPtNT>(ckey, cidx, (int)n, need, k, sh.rs, sh.sel, &sh.nsel, out);
 }
 
 }  // namespace

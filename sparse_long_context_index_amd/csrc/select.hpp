@@ -285,3 +285,89 @@ __device__ __forceinline__ uint32_t ordered_keep(const KeyAt& key_at, int n, uin
 }
 
 }  // namespace dsa
+
+namespace dsa {
+
+// Sorts the `need` indices in sel[0 .. need) (sel holds DSA_TOPK_MAX words)
+// ascending and writes them to out[0 .. k), padded with -1.  All NT threads
+// call it after the indices are in place; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void sort_emit(uint32_t* sel, uint32_t need, int k, int32_t* out) {
+  constexpr int kSortN = DSA_TOPK_MAX;
+  for (uint32_t i = need + threadIdx.x; i < (uint32_t)kSortN; i += NT) sel[i] = 0xFFFFFFFFu;
+  // bitonic sort of the kSortN slots, ascending
+  for (int size = 2; size <= kSortN; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < kSortN / 2; i += NT) {
+        const int a = 2 * i - (i & (stride - 1));
+        const int b = a + stride;
+        const uint32_t x = sel[a], y = sel[b];
+        const bool up = (a & size) == 0;
+        if ((x > y) == up) {
+          sel[a] = y;
+          sel[b] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += NT) out[j] = j < (int)need ? (int32_t)sel[j] : -1;
+  __syncthreads();
+}
+
+// Writes the indices of the set bits of bm[0 .. nw) in ascending order to
+// out[0 .. k), padded with -1: every thread counts the bits of a run of
+// words, one prefix sum places the runs.  All NT threads call it after the
+// bits are set; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void bitmap_emit(const uint32_t* bm, int nw, uint32_t* scan_sm, int k, int32_t* out) {
+  const int per = (nw + NT - 1) / NT;
+  const int w0 = (int)threadIdx.x * per;
+  const int w1 = w0 + per < nw ? w0 + per : nw;
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += (uint32_t)__popc(bm[w]);
+  uint32_t tot;
+  uint32_t pos = block_excl_scan<NT>(c, scan_sm, &tot);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t x = bm[w];
+    while (x) {
+      const int b = __builtin_ctz(x);
+      x &= x - 1u;
+      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
+      ++pos;
+    }
+  }
+  for (uint32_t j = tot + threadIdx.x; j < (uint32_t)k; j += NT) out[j] = -1;
+  __syncthreads();
+}
+
+// The exact top `need` (need <= DSA_TOPK_MAX) of n candidates (order keys
+// ckey[i] > 0, key indices cidx[i]) by (key desc, index asc), written to
+// out[0 .. k) in ascending index order and padded with -1.  The threshold
+// key and, among keys equal to it, the largest kept index come from radix
+// descents; the kept indices are collected in sel (DSA_TOPK_MAX words) and
+// sorted there.  All NT threads call it; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void select_sorted(const uint32_t* ckey, const uint32_t* cidx, int n, uint32_t need,
+                                              int k, RadixShared& rs, uint32_t* sel, uint32_t* nsel,
+                                              int32_t* out) {
+  if (threadIdx.x == 0) *nsel = 0;
+  uint32_t tau, r, eq;
+  radix_threshold<NT>([&](int i) { return ckey[i]; }, n, need, rs, &tau, &r, &eq);
+  // among tau-equal entries the r lowest indices win: threshold on ~index
+  uint32_t imax = 0xFFFFFFFFu;
+  if (eq > r) {
+    uint32_t tau2, r2, eq2;
+    radix_threshold<NT>([&](int i) { return ckey[i] == tau ? ~cidx[i] : 0u; }, n, r, rs, &tau2, &r2, &eq2);
+    imax = ~tau2;
+  }
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t key = ckey[i], id = cidx[i];
+    if (key > tau || (key == tau && id <= imax)) sel[atomicAdd(nsel, 1u)] = id;
+  }
+  __syncthreads();
+  sort_emit<NT>(sel, need, k, out);
+}
+
+}  // namespace dsa

@@ -42,6 +42,7 @@ constexpr int kCandCap = 16384;                                 // LDS candidate
 constexpr int kHistRange = 2048;                                // per hist block
 constexpr int kRowThreads = 1024;
 constexpr int kRowCap = 6144;                                   // LDS candidates per row
+constexpr int kRowReps = 8;                                     // level-1 histogram copies (lane l uses l % 8)
 
 // Sources of candidates for the final pass, walked in ascending index order
 // as nseg() consecutive segments.  get() returns (key, index); key 0 marks an
@@ -362,30 +363,72 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
 
 // ------------------------------------------------------------ row path
 
+// Per row: the level-1 histogram of the order keys (in kRowReps copies:
+// scores of one row fall into few level-1 bins, and LDS atomics on one
+// address serialise; lane l counts into copy l % kRowReps, the copies' rows
+// padded so that copies of one bin sit in different banks), its threshold
+// bin b1, then every key at or above the bin is a candidate: each wave
+// appends its candidates to a region of its own (positions from its ballots,
+// no atomics), unused slots hold key 0.  The
+// exact top k of the candidates is resolved and emitted in index order by
+// select_sorted.  A row whose candidates overflow the LDS slots takes the
+// ordered full-row path of final_select instead (same result, slower).
+constexpr int kRepStride = kHistBins + 4;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kWaveCap = kRowCap / kRowWaves;                   // candidate slots per wave
+
+// The smallest float whose order key is at least K: the candidate tests of
+// the row kernel compare the scores themselves.  Keys at or below that of
+// -inf map to -inf, keys above that of +inf to +inf.
+__device__ __forceinline__ float key_floor(uint32_t K) {
+  if (K <= 0x007FFFFFu) return -INFINITY;
+  if (K >= 0xFF800000u) return INFINITY;
+  return __uint_as_float((K & 0x80000000u) ? (K & 0x7FFFFFFFu) : ~K);
+}
+
+struct RowCand {
+  uint32_t key[kRowCap];
+  uint32_t idx[kRowCap];
+};
+
+union RowShared {
+  uint32_t rep[kRowReps * kRepStride];
+  RowCand c;
+};
+
+struct RowSel {
+  RadixShared rs;
+  uint32_t sel[DSA_TOPK_MAX];
+  uint32_t nsel, count;
+  uint32_t wcount[kRowWaves];
+};
+
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                                int64_t Lk, int T, int k,
                                                                int32_t* __restrict__ idx, SeqBatch sb,
                                                                int32_t* __restrict__ idx_rows) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-  __shared__ uint2 cand[kRowCap];
+  __shared__ __attribute__((aligned(16))) RowShared rsh;
+  __shared__ __attribute__((aligned(16))) RowSel sh;
   __shared__ FinalShared fs;
-  __shared__ uint32_t s_b1, s_above1;
   const int t = blockIdx.x;
   int64_t first = 0;
   if (sb.len) Lk = seq_keys(sb, t / T, &first);        // batch: row t is token t % T of sequence t / T
   const int tt = sb.len ? t % T : t;
   int64_t n = Lk - T + tt + 1;
   n = n > 0 ? n : 0;
-  const bool all_mode = n <= (int64_t)k;
   const float* row = scores + (int64_t)t * ld;
   int32_t* out_row = idx + (size_t)t * k;
+  const int lane = threadIdx.x & 63;
 
-  uint32_t b1 = 0, k1 = 0;
-  if (!all_mode) {
-    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;
+  if (n <= (int64_t)k) {
+    // every visible key is kept
+    for (int j = threadIdx.x; j < k; j += kRowThreads) out_row[j] = j < n ? j : -1;
+  } else {
+    // ---- level-1 histogram
+    for (int i = threadIdx.x; i < kRowReps * kRepStride; i += kRowThreads) rsh.rep[i] = 0;
     __syncthreads();
-    // 32 independent loads in flight per thread
-    constexpr int kH = 32;
+    uint32_t* hrep = rsh.rep + (lane % kRowReps) * kRepStride;
+    constexpr int kH = 32;                             // independent loads in flight per thread
     for (int64_t s0 = threadIdx.x; s0 < n; s0 += kH * kRowThreads) {
       float v[kH];
 #pragma unroll
@@ -395,69 +438,120 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       }
 #pragma unroll
       for (int e = 0; e < kH; ++e)
-        if (s0 + (int64_t)e * kRowThreads < n) atomicAdd(&hist[order_key(v[e]) >> 20], 1u);
+        if (s0 + (int64_t)e * kRowThreads < n) atomicAdd(&hrep[order_key(v[e]) >> 20], 1u);
     }
     __syncthreads();
-    find_threshold_bin<kRowThreads, kHistBins>(hist, (uint32_t)k, fs.scan, &s_b1, &s_above1);
-    b1 = s_b1;
-    k1 = (uint32_t)k - s_above1;
-    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) hist[i] = 0;   // becomes h2
-    __syncthreads();
-  }
-  // ordered compaction of candidates (level-1 digit >= b1) into LDS.  A
-  // round covers kPer * kRowThreads elements, element base + e * kRowThreads
-  // + tid in thread tid (coalesced loads, all issued first); positions follow
-  // the index order (e, wave, lane): per-(e, wave) counts from the ballots,
-  // one scan over them, then each lane's rank in its ballot.
-  constexpr int kPer = 24;
-  constexpr int kW = kRowThreads / 64;
-  __shared__ uint32_t woff[kPer * kW];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t count = 0;
-  for (int64_t base = 0; base < n; base += (int64_t)kPer * kRowThreads) {
-    uint32_t key[kPer];
+    for (int i = 4 * threadIdx.x; i < kHistBins; i += 4 * kRowThreads) {
+      uint4 sum = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
-      key[e] = __float_as_uint(row[s < n ? s : n - 1]);
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
-      key[e] = s < n ? order_key(__uint_as_float(key[e])) : 0u;
-      const bool f = s < n && (key[e] >> 20) >= b1;
-      if (f && !all_mode && (key[e] >> 20) == b1) atomicAdd(&hist[(key[e] >> 8) & 0xFFF], 1u);
-      const uint64_t m = __ballot(f);
-      if (lane == e) woff[e * kW + wv] = (uint32_t)__builtin_popcountll(m);
+      for (int r = 0; r < kRowReps; ++r) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&rsh.rep[r * kRepStride + i]);
+        sum.x += q.x;
+        sum.y += q.y;
+        sum.z += q.z;
+        sum.w += q.w;
+      }
+      *reinterpret_cast<uint4*>(&sh.rs.hist[i]) = sum;
     }
     __syncthreads();
-    uint32_t tot;
-    const uint32_t x = threadIdx.x < kPer * kW ? woff[threadIdx.x] : 0u;
-    const uint32_t off = block_excl_scan<kRowThreads>(x, fs.scan, &tot);
-    if (threadIdx.x < kPer * kW) woff[threadIdx.x] = off;
+    find_threshold_bin<kRowThreads, kHistBins>(sh.rs.hist, (uint32_t)k, fs.scan, &sh.rs.bin, &sh.rs.above);
+    const uint32_t b1 = sh.rs.bin, above1 = sh.rs.above;
+    // ---- candidates: keys whose level-1 digit is >= b1 (the copies are
+    // dead); the level-2 digits of the boundary bin's keys go to h2, which
+    // lies past the candidate slots
+    uint32_t* h2 = rsh.rep + 2 * kRowCap;
+    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) h2[i] = 0;
     __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int wv = threadIdx.x >> 6;
+    uint32_t* wkey = rsh.c.key + wv * kWaveCap;
+    uint32_t* widx = rsh.c.idx + wv * kWaveCap;
+    uint32_t wcnt = 0;                                 // wave-uniform
+    const float flo = key_floor(b1 << 20);             // level-1 digit >= b1 <=> score >= flo
+    const float fhi = b1 == 0xFFFu ? INFINITY : key_floor((b1 + 1u) << 20);   // +inf: test the digit
+    for (int64_t s0 = threadIdx.x; s0 < n; s0 += kH * kRowThreads) {
+      float v[kH];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
-      const bool f = s < n && (key[e] >> 20) >= b1;
-      const uint64_t m = __ballot(f);
-      if (f) {
-        const uint32_t p = count + woff[e * kW + wv] + (uint32_t)__builtin_popcountll(m & below);
-        if (p < kRowCap) cand[p] = make_uint2(key[e], (uint32_t)s);
+      for (int e = 0; e < kH; ++e) {
+        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        v[e] = row[s < n ? s : n - 1];
+      }
+#pragma unroll
+      for (int e = 0; e < kH; ++e) {
+        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        const bool f = s < n && v[e] >= flo;
+        const uint64_t m = __ballot(f);
+        if (f) {
+          const uint32_t key = order_key(v[e]);
+          if (fhi == INFINITY ? (key >> 20) == b1 : v[e] < fhi) atomicAdd(&h2[(key >> 8) & 0xFFF], 1u);
+          const uint32_t pos = wcnt + (uint32_t)__popcll(m & below);
+          if (pos < (uint32_t)kWaveCap) {
+            wkey[pos] = key;
+            widx[pos] = (uint32_t)s;
+          }
+        }
+        wcnt += (uint32_t)__popcll(m);
       }
     }
-    count += tot;
-    __syncthreads();                                   // woff is rewritten by the next round
-  }
-  __syncthreads();
-  if (count <= kRowCap) {
-    FlatSource src{cand, (int)count, kRowThreads};
-    final_select<kRowThreads>(src, k, all_mode, b1, k1, hist, fs, out_row);
-  } else {
-    const int64_t seg = (n + kRowThreads - 1) / kRowThreads;
-    RowSource src{row, n, seg, kRowThreads, all_mode ? 0u : b1};
-    final_select<kRowThreads>(src, k, all_mode, b1, k1, hist, fs, out_row);
+    for (uint32_t i = wcnt + lane; i < (uint32_t)kWaveCap; i += 64) wkey[i] = 0u;   // unused slots
+    if (lane == 0) sh.wcount[wv] = wcnt;
+    __syncthreads();
+    bool fits = true;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) fits &= sh.wcount[w] <= (uint32_t)kWaveCap;
+    const uint32_t count = kRowCap;                    // slots, the unused ones with key 0
+    if (fits) {
+      // threshold key tau: level 2 from h2, level 3 over the candidates
+      const uint32_t* ck = rsh.c.key;
+      const uint32_t* ci = rsh.c.idx;
+      find_threshold_bin<kRowThreads, kHistBins>(h2, (uint32_t)k - above1, fs.scan, &fs.bin, &fs.above);
+      const uint32_t b2 = fs.bin;
+      const uint32_t k2 = (uint32_t)k - above1 - fs.above;
+      for (int i = threadIdx.x; i < kHist3Bins; i += kRowThreads) fs.h3[i] = 0;
+      __syncthreads();
+      const uint32_t pre = (b1 << 12) | b2;           // key bits 31..8 of the boundary
+      for (uint32_t i = threadIdx.x; i < count; i += kRowThreads)
+        if (ck[i] && (ck[i] >> 8) == pre) atomicAdd(&fs.h3[ck[i] & 0xFF], 1u);
+      __syncthreads();
+      find_threshold_bin<kRowThreads, kHist3Bins>(fs.h3, k2, fs.scan, &fs.bin, &fs.above);
+      const uint32_t tau = (pre << 8) | fs.bin;
+      const uint32_t r = k2 - fs.above;                // tau-equal keys to keep: the r lowest indices
+      const uint32_t eq = fs.h3[fs.bin];
+      uint32_t imax = 0xFFFFFFFFu;
+      if (eq > r) {                                    // block-uniform
+        uint32_t tau2, r2, eq2;
+        radix_threshold<kRowThreads>([&](int i) { return ck[i] == tau ? ~ci[i] : 0u; }, (int)count, r, sh.rs,
+                                     &tau2, &r2, &eq2);
+        imax = ~tau2;
+      }
+      // the kept set in index order: a bitmap over the row when it fits in
+      // sel, else the sort
+      const int nw = (int)((n + 31) / 32);
+      if (nw <= DSA_TOPK_MAX) {
+        for (int i = threadIdx.x; i < nw; i += kRowThreads) sh.sel[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < count; i += kRowThreads) {
+          const uint32_t key = ck[i], id = ci[i];
+          if (key > tau || (key == tau && id <= imax)) atomicOr(&sh.sel[id >> 5], 1u << (id & 31));
+        }
+        __syncthreads();
+        bitmap_emit<kRowThreads>(sh.sel, nw, fs.scan, k, out_row);
+      } else {
+        if (threadIdx.x == 0) sh.nsel = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < count; i += kRowThreads) {
+          const uint32_t key = ck[i], id = ci[i];
+          if (key > tau || (key == tau && id <= imax)) sh.sel[atomicAdd(&sh.nsel, 1u)] = id;
+        }
+        __syncthreads();
+        sort_emit<kRowThreads>(sh.sel, (uint32_t)k, k, out_row);
+      }
+    } else {
+      // overflow: the ordered pass over the row
+      const int64_t seg = (n + kRowThreads - 1) / kRowThreads;
+      RowSource src{row, n, seg, kRowThreads, b1};
+      final_select<kRowThreads>(src, k, false, b1, (uint32_t)k - above1, h2, fs, out_row);
+    }
   }
   if (idx_rows) {
     // the same set as cache rows of the sequence
