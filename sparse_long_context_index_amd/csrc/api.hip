@@ -327,7 +327,7 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
     return hip_status(launch_attn_merge(d.a, d.n_chunks, d.part, st));
   }
   // up to kScanHistTMax tokens the scan also builds the top-k's level-1 histogram
-  const bool fused = T <= kScanHistTMax && topk_multi_block(Lk, T);
+  const bool fused = T <= kScanHistTMax && topk_multi_block(Lk, T, k);
   hipError_t e = launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld, st, fused ? base : nullptr);
   if (e != hipSuccess) return DSA_ERR_HIP;
   e = launch_topk(scores, ld, Lk, T, k, idx, base, base + L.topk, st, fused);

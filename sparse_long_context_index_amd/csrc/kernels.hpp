@@ -59,7 +59,7 @@ hipError_t launch_index_scores_batch(const uint8_t* q_idx, const float* w, const
 
 // ---- top-k
 size_t topk_scratch_bytes(int64_t Lk, int T, int k);
-bool topk_multi_block(int64_t Lk, int T);   // few long rows: the multi-block path
+bool topk_multi_block(int64_t Lk, int T, int k);   // few long rows: the multi-block path
 // hist_ready: the level-1 histogram of these scores is already in the counter
 // region (built by the scan); otherwise launch_topk builds it first.
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,

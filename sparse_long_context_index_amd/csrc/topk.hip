@@ -90,6 +90,19 @@ struct FlatSource {      // an ordered candidate array (LDS, row kernel)
   __device__ uint2 get(int w, int i) const { return a[w * ((n + G - 1) / G) + i]; }
 };
 
+// Row t of a launch: its visible keys and, for a batch (row t is token t % T
+// of sequence t / T), the first cache row of its sequence.
+__device__ __forceinline__ int64_t row_keys(const SeqBatch& sb, int64_t Lk, int T, int t, int64_t* first) {
+  int64_t n;
+  if (sb.len) {
+    n = seq_keys(sb, t / T, first) - T + t % T + 1;
+  } else {
+    *first = 0;
+    n = Lk - T + t + 1;
+  }
+  return n > 0 ? n : 0;
+}
+
 struct FinalShared {
   uint32_t scan[1024 / 64];
   uint32_t h3[kHist3Bins];
@@ -219,7 +232,8 @@ __device__ void find_b1(const TopkCounters& ctr, int t, uint32_t need, uint32_t*
 // so the compaction offsets come from per-wave ballots and one 64-entry scan.
 __global__ __launch_bounds__(256) void topk_collect_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
-    uint2* __restrict__ slots, uint32_t* __restrict__ slot_cnt, uint32_t* __restrict__ rowinfo, int G) {
+    uint2* __restrict__ slots, uint32_t* __restrict__ slot_cnt, uint32_t* __restrict__ rowinfo, int G,
+    SeqBatch sb) {
   __shared__ uint32_t h2[kHistBins];
   __shared__ uint32_t scan_sm[4];
   __shared__ uint32_t wcnt[kCollectPer * 4];
@@ -228,8 +242,10 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t n = Lk - T + t + 1;
+  int64_t first;
+  const int64_t n = row_keys(sb, Lk, T, t, &first);
   const bool all_mode = n <= (int64_t)k;
+  if (all_mode) return;                                  // the final kernel keeps every visible key
   const float* row = scores + (int64_t)t * ld;
   const int64_t lo = (int64_t)wg * kCollectRange + threadIdx.x;
 
@@ -313,7 +329,7 @@ struct FinalKernelShared {
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t Lk, int T, int k, TopkCounters ctr,
     const uint2* __restrict__ slots, const uint32_t* __restrict__ slot_cnt, const uint32_t* __restrict__ rowinfo,
-    int G, int32_t* __restrict__ idx) {
+    int G, int32_t* __restrict__ idx, SeqBatch sb, int32_t* __restrict__ idx_rows) {
   __shared__ FinalKernelShared sh;
   const int t = blockIdx.x;
   if (blockIdx.y > 0) {
@@ -323,10 +339,22 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     if (threadIdx.x == 0) ctr.maxbin[r * kMaxCounterRows + t] = 0;
     return;
   }
-  const int64_t n = Lk - T + t + 1;
+  int64_t first;
+  const int64_t n = row_keys(sb, Lk, T, t, &first);
   const bool all_mode = n <= (int64_t)k;
   const float* row = scores + (int64_t)t * ld;
   int32_t* out_row = idx + (size_t)t * k;
+  if (all_mode) {
+    // every visible key is kept (the collect kernel skipped the row)
+    for (int j = threadIdx.x; j < k; j += kFinalThreads) {
+      out_row[j] = j < n ? j : -1;
+      if (idx_rows) idx_rows[(size_t)t * k + j] = j < n ? (int32_t)(first + j) : -1;
+    }
+    uint4* z2 = reinterpret_cast<uint4*>(ctr.h2 + (size_t)t * kHistBins);
+    for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z2[i] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x == 0) ctr.overflow[t] = 0;
+    return;
+  }
   // every independent load first
   const uint32_t ovf = ctr.overflow[t];
   const uint32_t b1 = all_mode ? 0u : rowinfo[2 * t];
@@ -359,6 +387,13 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   uint4* z2 = reinterpret_cast<uint4*>(ctr.h2 + (size_t)t * kHistBins);
   for (int i = threadIdx.x; i < kHistBins / 4; i += kFinalThreads) z2[i] = make_uint4(0, 0, 0, 0);
   if (threadIdx.x == 0) ctr.overflow[t] = 0;
+  if (idx_rows) {
+    // the same set as cache rows of the sequence
+    for (int j = threadIdx.x; j < k; j += kFinalThreads) {
+      const int32_t v = out_row[j];
+      idx_rows[(size_t)t * k + j] = v >= 0 ? (int32_t)(first + v) : -1;
+    }
+  }
 }
 
 // ------------------------------------------------------------ row path
@@ -563,23 +598,26 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   }
 }
 
-bool multi_block(int64_t Lk, int T) {
-  return T <= kTopkMultiRowsMax && cdiv(Lk, kCollectRange) <= kMaxSegs;
+// Few long rows take the multi-block path: enough blocks that a row's
+// candidates (about k plus the boundary bin) spread well within the blocks'
+// slots; shorter rows are served by one workgroup each.
+bool multi_block(int64_t Lk, int T, int k) {
+  const int64_t G = cdiv(Lk, kCollectRange);
+  return T <= kTopkMultiRowsMax && G <= kMaxSegs && G * kSlotCap >= (int64_t)4 * k;
 }
 
 }  // namespace
 
 
 size_t topk_scratch_bytes(int64_t Lk, int T, int k) {
-  (void)k;
-  if (!multi_block(Lk, T)) return 256;
+  if (!multi_block(Lk, T, k)) return 256;
   const int64_t G = cdiv(Lk, kCollectRange);
   return (size_t)T * G * kSlotCap * sizeof(uint2) + (size_t)T * G * sizeof(uint32_t) + (size_t)T * 8 + 256;
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k, int32_t* idx,
                        void* ws_counters, void* scratch, hipStream_t st, bool hist_ready) {
-  if (!multi_block(Lk, T)) {
+  if (!multi_block(Lk, T, k)) {
     hipLaunchKernelGGL(topk_row_kernel, dim3(T), dim3(kRowThreads), 0, st, scores, ld, Lk, T, k, idx, SeqBatch{},
                        (int32_t*)nullptr);
     return hipGetLastError();
@@ -597,15 +635,16 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)G, T), dim3(256), 0, st, scores, ld, Lk, T, k, ctr,
-                     slots, cnt, rowinfo, (int)G);
+                     slots, cnt, rowinfo, (int)G, SeqBatch{});
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_final_kernel, dim3(T, 1 + kHistReplicas), dim3(kFinalThreads), 0, st, scores, ld, Lk, T,
-                     k, ctr, (const uint2*)slots, (const uint32_t*)cnt, (const uint32_t*)rowinfo, (int)G, idx);
+                     k, ctr, (const uint2*)slots, (const uint32_t*)cnt, (const uint32_t*)rowinfo, (int)G, idx,
+                     SeqBatch{}, (int32_t*)nullptr);
   return hipGetLastError();
 }
 
-bool topk_multi_block(int64_t Lk, int T) { return multi_block(Lk, T); }
+bool topk_multi_block(int64_t Lk, int T, int k) { return multi_block(Lk, T, k); }
 
 hipError_t launch_topk_batch(const float* scores, int64_t ld, const SeqBatch& sb, int B, int T, int k, int32_t* idx,
                              int32_t* idx_rows, hipStream_t st) {
