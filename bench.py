@@ -19,6 +19,8 @@ Printed (one JSON line):
   cache_append     the step that appends new tokens to the caches (LayerNorm,
             partial RoPE, fp8/bf16 rounding, cache writes): one decode token,
             and a full 8,192-token prefill chunk as HBM GB/s
+  small_decode     the 8K-key decode step and the 4-token verify at 128K
+            (latency per step; their caches stay in the Infinity Cache)
   cpu_baseline     the fp64 oracle's decode step on this host, on a bounded
             sample, in the same unit
 """
@@ -66,6 +68,7 @@ def parse():
     ap.add_argument("--no-batch", action="store_true")
     ap.add_argument("--no-recall", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=10)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run 4 plain device copies of this many bytes (calibrates HBM counters)")
@@ -178,6 +181,8 @@ def main():
         result["index_recall"] = bench_recall(torch, binding, dev, inst[0], sm, reps)
     if not args.no_swa:
         result["swa_decode"] = bench_swa(torch, np, binding, synth, dev, reps)
+    if not args.no_small:
+        result["small_decode"] = bench_small(torch, np, binding, synth, dev, reps)
     if not args.no_prefill:
         del scores
         result["prefill_indexer"] = bench_prefill(torch, np, binding, synth, dev)
@@ -342,6 +347,46 @@ def bench_append(torch, binding, dev, x, reps):
                         "bytes": nbytes, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"},
             "bytes_per_token": APPEND_BYTES_PER_TOKEN}
+
+
+def decode_step_bytes(Lk, T, k):
+    """Algorithmic bytes of one decode step: every visible index key, the
+    gathered K/V of each token's k keys, queries, outputs, index queries,
+    weights and the sink."""
+    return (Lk * 128 + T * k * 4 * (192 + 128) * 2 + T * (64 * 192 * 2 + 64 * 128 * 2 + 16 * 128 + 16 * 4)
+            + 64 * 4)
+
+
+def bench_small(torch, np, binding, synth, dev, reps):
+    """The two smaller decode workloads (8K-key history, one token; the
+    4-token verify at 128K), one step per graph launch replayed.  Their index
+    caches (1 MB, 16 MB) stay in the 256 MB Infinity Cache between replays,
+    so the rates are latency figures, not HBM bandwidth."""
+    out = {}
+    for name in ("dsa_decode_8k", "dsa_verify_128k_t4"):
+        cfg = synth.CONFIGS[name]
+        d = synth.decode_inputs(cfg)
+        x = {}
+        for n in ("q_idx", "w", "k_idx", "q", "k", "v", "sink"):
+            a = np.ascontiguousarray(d[n])
+            x[n] = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        ws = binding.Workspace(binding.workspace_bytes(binding.OP_DECODE_STEP, cfg.Lk, cfg.T, cfg.k))
+        o = torch.empty((cfg.T, 64, 128), dtype=torch.bfloat16, device=dev)
+        sm = float(d["sm_scale"])
+
+        def f():
+            binding.dsa_decode_step(x["q_idx"], x["w"], x["k_idx"], x["q"], x["k"], x["v"], cfg.Lk, cfg.T, cfg.k,
+                                    x["sink"], sm, out=o, ws=ws)
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        g = capture(torch, lambda: [f() for _ in range(8)])
+        ms = replay_ms(torch, g, max(reps // 8, 10))[0] / 8
+        nbytes = decode_step_bytes(cfg.Lk, cfg.T, cfg.k)
+        out[name] = {"history": cfg.L, "query_tokens": cfg.T, "topk": cfg.k, "us": round(ms * 1e3, 3),
+                     "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+        del x, ws, o
+    return out
 
 
 def bench_batch(torch, np, binding, synth, dev, reps, B=64):

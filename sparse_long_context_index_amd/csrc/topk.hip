@@ -460,20 +460,28 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     for (int j = threadIdx.x; j < k; j += kRowThreads) out_row[j] = j < n ? j : -1;
   } else {
     // ---- level-1 histogram
-    for (int i = threadIdx.x; i < kRowReps * kRepStride; i += kRowThreads) rsh.rep[i] = 0;
+    static_assert((kRowReps * kRepStride) % 4 == 0, "16-byte clears");
+    for (int i = threadIdx.x; i < kRowReps * kRepStride / 4; i += kRowThreads)
+      reinterpret_cast<uint4*>(rsh.rep)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     uint32_t* hrep = rsh.rep + (lane % kRowReps) * kRepStride;
-    constexpr int kH = 32;                             // independent loads in flight per thread
-    for (int64_t s0 = threadIdx.x; s0 < n; s0 += kH * kRowThreads) {
+    // Rounds of kH scores per thread (score base + e * kRowThreads + thread),
+    // all loads issued first; groups of 8 that start past the row are skipped
+    // (the test is uniform over the workgroup).
+    constexpr int kH = 32;
+    for (int64_t base = 0; base < n; base += (int64_t)kH * kRowThreads) {
       float v[kH];
 #pragma unroll
       for (int e = 0; e < kH; ++e) {
-        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        if (e % 8 == 0 && base + (int64_t)e * kRowThreads >= n) break;
+        const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
         v[e] = row[s < n ? s : n - 1];
       }
 #pragma unroll
-      for (int e = 0; e < kH; ++e)
-        if (s0 + (int64_t)e * kRowThreads < n) atomicAdd(&hrep[order_key(v[e]) >> 20], 1u);
+      for (int e = 0; e < kH; ++e) {
+        if (e % 8 == 0 && base + (int64_t)e * kRowThreads >= n) break;
+        if (base + (int64_t)e * kRowThreads + threadIdx.x < n) atomicAdd(&hrep[order_key(v[e]) >> 20], 1u);
+      }
     }
     __syncthreads();
     for (int i = 4 * threadIdx.x; i < kHistBins; i += 4 * kRowThreads) {
@@ -504,16 +512,18 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     uint32_t wcnt = 0;                                 // wave-uniform
     const float flo = key_floor(b1 << 20);             // level-1 digit >= b1 <=> score >= flo
     const float fhi = b1 == 0xFFFu ? INFINITY : key_floor((b1 + 1u) << 20);   // +inf: test the digit
-    for (int64_t s0 = threadIdx.x; s0 < n; s0 += kH * kRowThreads) {
+    for (int64_t base = 0; base < n; base += (int64_t)kH * kRowThreads) {
       float v[kH];
 #pragma unroll
       for (int e = 0; e < kH; ++e) {
-        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        if (e % 8 == 0 && base + (int64_t)e * kRowThreads >= n) break;
+        const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
         v[e] = row[s < n ? s : n - 1];
       }
 #pragma unroll
       for (int e = 0; e < kH; ++e) {
-        const int64_t s = s0 + (int64_t)e * kRowThreads;
+        if (e % 8 == 0 && base + (int64_t)e * kRowThreads >= n) break;
+        const int64_t s = base + (int64_t)e * kRowThreads + threadIdx.x;
         const bool f = s < n && v[e] >= flo;
         const uint64_t m = __ballot(f);
         if (f) {
