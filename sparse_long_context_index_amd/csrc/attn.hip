@@ -53,28 +53,42 @@ __global__ __launch_bounds__(NW * 64) void swa_attn_kernel(AttnArgs a, int n_chu
   attend_chunk<HKV, NW>(a, src, b, g, c, n_chunks, p0 < p1 ? p0 : p1, p1, part, smem);
 }
 
-// merge the chunk partials of every (t, head) and add the sink; every load is
-// issued before any is used
+// merge the chunk partials of every (t, head) and add the sink.  All loads
+// go out together as vector loads: lane c of each wave fetches chunk c's
+// (max, sum) and the sink, and the values are then read across the wave, so
+// the kernel waits for one memory round trip.
 constexpr int kMaxChunks = 32;
 
 template <int HKV, int MAXC>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_chunks, const float* part) {
+  static_assert(MAXC <= 64, "one chunk per lane");
   constexpr int GH = 64 / HKV;
   const int h = blockIdx.x, t = blockIdx.y;
   const int g = h / GH, hc = h % GH;
   const int dv = threadIdx.x;
+  const int lane = dv & 63;
   const float* pp = part + ((size_t)(t * HKV + g) * n_chunks) * kPartFloats;
-  float mc[MAXC], lc[MAXC], oc[MAXC];
+  const int cl = lane < n_chunks ? lane : 0;                   // chunk 0 stands in beyond n_chunks
+  const float ml = pp[(size_t)cl * kPartFloats + hc];
+  const float ll = pp[(size_t)cl * kPartFloats + 16 + hc];
+  // lane 63 fetches the sink (a lane-dependent address keeps it a vector load
+  // issued with the others); the other lanes re-read a word of the partials
+  const float sl = *((a.sink && lane == 63) ? a.sink + h : pp + hc);
+  float oc[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const float* q = pp + (size_t)(c < n_chunks ? c : 0) * kPartFloats;
+    oc[c] = q[32 + hc * 128 + dv];                             // loaded unconditionally, masked below
+  }
+  float mc[MAXC], lc[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     const bool ok = c < n_chunks;
-    const float* q = pp + (size_t)(ok ? c : 0) * kPartFloats;   // chunk 0 stands in beyond n_chunks
-    const float m = q[hc], l = q[16 + hc], o = q[32 + hc * 128 + dv];
-    mc[c] = ok ? m : -INFINITY;
-    lc[c] = ok ? l : 0.f;
-    oc[c] = ok ? o : 0.f;
+    mc[c] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml), c)) : -INFINITY;
+    lc[c] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), c)) : 0.f;
+    oc[c] = ok ? oc[c] : 0.f;
   }
-  const float s2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+  const float s2 = a.sink ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl), 63)) * kLog2e : -INFINITY;
   float M = s2;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) M = fmaxf(M, mc[c]);

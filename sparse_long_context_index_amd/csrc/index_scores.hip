@@ -204,9 +204,40 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
     int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist, ScanLists lists, SeqBatch sb) {
+  int64_t wg = blockIdx.x, G = gridDim.x;                      // this workgroup among its row's, and their number
   if (!kLists && sb.len) {
-    // batch: grid dimension y is the sequence; its keys, queries and score rows
-    const int b = blockIdx.y;
+    // batch: the sequence b, its keys, queries and score rows
+    int b = blockIdx.y;
+    if (sb.spread) {
+      // Workgroups dealt by length: every workgroup derives the same deal from
+      // the lengths -- sequence i (ng_i key groups of N in all) gets 1 +
+      // floor(768 ng_i / N) workgroups, at most ng_i, in sequence order --
+      // and takes its place in it; the grid has 768 + B workgroups, enough for
+      // any deal.  Grid dimension y is 1.
+      __shared__ uint32_t deal_sm[4];
+      __shared__ int64_t deal_out[3];
+      int64_t f0;
+      const int64_t n_i = (int)threadIdx.x < sb.spread ? seq_keys(sb, threadIdx.x, &f0) : 0;
+      const uint32_t ng = (uint32_t)cdiv(cdiv(n_i, 16), 4 * kScanUnroll);
+      uint32_t N, used;
+      (void)block_excl_scan<256>(ng, deal_sm, &N);
+      uint32_t per = 0;
+      if (ng) {
+        per = 1u + (uint32_t)((uint64_t)kPlainScanBlocks * ng / N);
+        per = per < ng ? per : ng;
+      }
+      const uint32_t ex = block_excl_scan<256>(per, deal_sm, &used);
+      if (blockIdx.x >= used) return;                           // block-uniform: a spare workgroup
+      if (blockIdx.x >= ex && blockIdx.x < ex + per) {
+        deal_out[0] = threadIdx.x;
+        deal_out[1] = blockIdx.x - ex;
+        deal_out[2] = per;
+      }
+      __syncthreads();
+      b = (int)deal_out[0];
+      wg = deal_out[1];
+      G = deal_out[2];
+    }
     int64_t first;
     Lk = seq_keys(sb, b, &first);
     q_idx += (size_t)b * T * 16 * 128;
@@ -245,7 +276,6 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 
   const int64_t last = Lk - 1;
   const int64_t ntiles = cdiv(Lk, 16);
-  const int64_t G = gridDim.x;
   uint8_t* st = stage + wave * kScanUnroll * 16 * kStageRow;
   i32x4 buf[2 * kScanUnroll];
   // With lists, local tile lt of this workgroup is global tile blockIdx.x +
@@ -253,8 +283,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   // u; without, step `it` covers the group of 16 consecutive tiles blockIdx.x
   // + G * it, kScanUnroll of them per wave.  Load i covers 8 keys of tile i / 2.
   auto tile_of = [&](int it, int u) -> int64_t {
-    if (kLists) return (int64_t)blockIdx.x + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
-    return ((int64_t)blockIdx.x + G * (int64_t)it) * 4 * kScanUnroll + wave * kScanUnroll + u;
+    if (kLists) return wg + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
+    return (wg + G * (int64_t)it) * 4 * kScanUnroll + wave * kScanUnroll + u;
   };
   auto load_step = [&](int it) {
 #pragma unroll
@@ -265,8 +295,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     }
   };
 
-  const int n_steps = kLists ? (int)cdiv(cdiv(ntiles - blockIdx.x, G), 4 * kScanUnroll)
-                             : (int)cdiv(ngroups - blockIdx.x, G);
+  const int n_steps = kLists ? (int)cdiv(cdiv(ntiles - wg, G), 4 * kScanUnroll)
+                             : (int)cdiv(ngroups - wg, G);
   int iter = 0;
   if (n_steps > 0) load_step(0);
   for (; iter < n_steps; ++iter) {
@@ -455,13 +485,30 @@ hipError_t launch_index_scores_batch(const uint8_t* q_idx, const float* w, const
                                      int B, int T, float* scores, int64_t ld, hipStream_t st) {
   if (B < 1 || T < 1 || ld < sb.max_len || B > 65535) return hipErrorInvalidValue;
   if (T > kDecodeTMax) return launch_idx_gemm_batch(q_idx, w, k_idx, sb, B, T, scores, ld, st);
-  // per sequence a share of the plain scan's workgroups, at most its key groups
+  const size_t lds = scan_lds_bytes(sb.max_len, T, false);
+  const TopkCounters ctr{};
   const int64_t max_groups = cdiv(cdiv(sb.max_len, 16), 4 * kScanUnroll);
+  if (B <= 256) {
+    // workgroups dealt by length inside the kernel (768 + B, the spares exit)
+    SeqBatch sp = sb;
+    sp.spread = B;
+    switch (T) {
+#define DSA_SCAN_SPREAD(n)                                                                                  \
+  case n:                                                                                                   \
+    hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)(kPlainScanBlocks + B)), dim3(256), lds, st, \
+                       q_idx, w, k_idx, sb.max_len, scores, ld, max_groups, ctr, 0, ScanLists{}, sp);       \
+    break;
+      DSA_SCAN_SPREAD(1) DSA_SCAN_SPREAD(2) DSA_SCAN_SPREAD(3) DSA_SCAN_SPREAD(4)
+      DSA_SCAN_SPREAD(5) DSA_SCAN_SPREAD(6) DSA_SCAN_SPREAD(7) DSA_SCAN_SPREAD(8)
+#undef DSA_SCAN_SPREAD
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  // more sequences: per sequence a share of the plain scan's workgroups, at most its key groups
   int64_t per = cdiv(kPlainScanBlocks, B);
   per = per < max_groups ? per : max_groups;
   per = per < 1 ? 1 : per;
-  const size_t lds = scan_lds_bytes(sb.max_len, T, false);
-  const TopkCounters ctr{};
   switch (T) {
 #define DSA_SCAN_BATCH(n)                                                                                   \
   case n:                                                                                                   \

@@ -22,6 +22,7 @@ struct SeqBatch {
   const int32_t* len = nullptr;     // [B] device
   int64_t n_rows = 0;
   int64_t max_len = 0;
+  int32_t spread = 0;               // the batch scan: B when its workgroups are dealt by length (B <= 256)
 };
 
 // keys of sequence b (0 when its descriptor is invalid); *first receives its first row

@@ -135,3 +135,13 @@ def test_decode_batch_serving_workload(dev):
     o, idx, _ = run_batch(dev, seqs, 1, 2048, seed=5)
     for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 33):
         check_seq(dev, seqs[b], 1, 2048, o[b], idx[b], seqs[0]["sink"])
+
+
+def test_decode_batch_many_sequences(dev):
+    # more than 256 sequences: the scan gives each sequence a fixed share of
+    # workgroups instead of dealing them by length
+    lens = [int(n) for n in np.random.default_rng(9).integers(1, 3000, size=300)]
+    seqs = synth.batch_inputs(lens, 1, 256, seed=9)
+    o, idx, _ = run_batch(dev, seqs, 1, 256, seed=9)
+    for b in (0, 1, 150, int(np.argmax(lens)), 299):
+        check_seq(dev, seqs[b], 1, 256, o[b], idx[b], seqs[0]["sink"])
