@@ -312,12 +312,15 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
     sl.keys = reinterpret_cast<uint32_t*>(base + L.lkeys);
     sl.idx = reinterpret_cast<uint32_t*>(base + L.lidx);
     sl.count = reinterpret_cast<uint32_t*>(base + L.lcount);
+    sl.store_scores = scores_out != nullptr;     // else only a re-selection needs them, and recomputes them
     hipError_t e = launch_index_scores(q_idx, w, k_idx, Lk, T, scores, ld, st, nullptr, sl);
     if (e != hipSuccess) return DSA_ERR_HIP;
     DecodeArgs d{};
     d.a.q = q; d.a.k = k_cache; d.a.v = v_cache; d.a.n_rows = Lk; d.a.T = T; d.a.k_len = k;
     d.a.sink = sink; d.a.sm_scale = sm_scale; d.a.out = out; d.a.lse = lse;
     d.scores = scores; d.ld = ld; d.Lk = Lk; d.k = k;
+    d.rescore = sl.store_scores ? nullptr : scores;
+    d.q_idx = q_idx; d.w = w; d.k_idx = k_idx;
     d.lkeys = sl.keys; d.lidx = sl.idx; d.lcount = sl.count; d.nlists = scan_grid(Lk);
     d.idx_out = idx_out;
     d.part = reinterpret_cast<float*>(base + L.part);

@@ -17,7 +17,9 @@
 //   3. keeps from every list the prefix that precedes that entry, and checks
 //      that the union held the true top-k: when a capped list keeps its last
 //      entry, keys it dropped may belong to the top-k, and only then the
-//      workgroup re-selects from the whole scores row (same result, slower);
+//      workgroup re-selects from the whole scores row (same result, slower;
+//      when the caller asked for no scores the scan stored none, and the
+//      workgroup first recomputes the row);
 //   4. attends over its chunk of 128 kept keys for one KV head (the same tile
 //      loop as sparse_gqa_attn) and writes a partial (max, sum, output), or
 //      the output itself when one chunk covers the k keys.
@@ -28,6 +30,7 @@
 // 2,048 consecutive winners puts at most 16 in any one list.
 #include "attn_core.hpp"
 #include "dsa_common.hpp"
+#include "indexer.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -42,6 +45,44 @@ constexpr int kMaxLists = 512;
 constexpr int kLPT = kMaxLists / kDecNT;           // scan lists per thread
 constexpr int kDecMaxChunks = DSA_TOPK_MAX / kDecChunk;
 constexpr int kC1Cap = 64;                         // threshold-bin entries ranked directly
+
+// The scores of row t for keys 0 .. n_vis - 1, recomputed by this workgroup
+// into row with the scan's arithmetic (the same MFMA operands and order, so
+// the same bits) when the scan stored none.  Every workgroup of the row
+// writes the same values; the accesses are relaxed atomics, so the concurrent
+// writes of equal bits are well defined and a workgroup reads back its own.
+__device__ void rescore_row(const DecodeArgs& d, int t, int64_t n_vis, float* row) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 a[4];
+  float wv[4];
+  widen_fp8(load_frag32_cached(d.q_idx + (size_t)(t * 16 + col) * 128 + 32 * grp), a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = d.w[t * 16 + 4 * grp + i];
+  constexpr int U = 8;                                          // 16-key tiles per wave in flight
+  const int64_t ntiles = cdiv(n_vis, 16);
+  for (int64_t t0 = (int64_t)wave * U; t0 < ntiles; t0 += (int64_t)(kDecNT / 64) * U) {
+    i32x8 kr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = (t0 + u) * 16 + col;
+      kr[u] = load_frag32_cached(d.k_idx + (key < n_vis ? key : n_vis - 1) * 128 + 32 * grp);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = (t0 + u) * 16 + col;
+      bf16x8 b[4];
+      widen_fp8(kr[u], b);
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) c = mfma_bf16_16x16x32(a[k4], b[k4], c);
+      const float s = relu_weighted_sum(c, wv);
+      if (grp == 0 && key < n_vis)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(row) + key, __float_as_uint(s), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+}
 
 struct DecodeShared {
   union {
@@ -415,7 +456,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       if (n_sel > (uint32_t)DSA_TOPK_MAX) n_sel = DSA_TOPK_MAX;
     } else {
       const float* row = d.scores + (int64_t)t * d.ld;
-      auto row_key = [&](int i) { return order_key(row[i]); };
+      if (d.rescore) {
+        rescore_row(d, t, n_vis, d.rescore + (int64_t)t * d.ld);
+        __syncthreads();
+      }
+      auto row_key = [&](int i) {
+        return order_key(__uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(row) + i,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+      };
       uint32_t tau = 0, r = 0, eq = 0;
       if (n_vis > (int64_t)k) radix_threshold<kDecNT>(row_key, (int)n_vis, (uint32_t)k, sh.s.rs, &tau, &r, &eq);
       n_sel = ordered_keep<kDecNT>(row_key, (int)n_vis, tau, r, sh.scan,

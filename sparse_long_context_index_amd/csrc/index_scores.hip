@@ -43,18 +43,6 @@ __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   return r;
 }
 
-// 32 fp8 bytes -> four bf16x8 MFMA operands (k-step s takes bytes 8s..8s+7)
-__device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, false);
-    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, true);
-    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, false);
-    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, true);
-    out[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  }
-}
-
 // Decode scan.  Without lists, persistent workgroups (3 per CU) take groups
 // of 16 consecutive 16-key tiles in grid-stride order.  With lists, 16-key
 // tiles are dealt round-robin to the workgroups (tile j belongs to workgroup
@@ -79,7 +67,9 @@ __device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
 // into the workgroup's exact top kListM, written as a list sorted by (score
 // desc, index asc) of order keys and key indices, with a count word (bit 31:
 // more than kListM of its keys were visible).  The fused decode step selects
-// the global top-k from these lists.
+// the global top-k from these lists.  The scores themselves are stored only
+// when asked for (store_scores): the selection needs them only in its rare
+// re-selection, which can recompute them.
 constexpr int kStageRow = 144;                     // padded LDS bytes per 128-byte key row
 constexpr int kBufCap = 256;                       // wave buffer entries per row
 constexpr int kBufTrigger = kBufCap - 4 * 16;      // room for one more step of appends
@@ -342,7 +332,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
           bcnt[t] += (uint32_t)__popcll(m);
         }
       }
-      if (key < Lk) {
+      if (key < Lk && (!kLists || lists.store_scores)) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
           if ((t & 3) == grp) {

@@ -19,6 +19,18 @@ __device__ __forceinline__ i32x8 load_frag32_cached(const uint8_t* p) {
   return r;
 }
 
+// 32 fp8 bytes -> four bf16x8 MFMA operands (k-step s takes bytes 8s..8s+7)
+__device__ __forceinline__ void widen_fp8(const i32x8& r, bf16x8* out) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, false);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s], 1.0f, true);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, false);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)r[2 * s + 1], 1.0f, true);
+    out[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+}
+
 // Sum over the four 16-lane rows of the wave, in the order (r0 + r1) + (r2 +
 // r3), on the VALU: permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap
 // the two halves; every lane ends with the same bits.

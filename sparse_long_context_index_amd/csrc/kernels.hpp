@@ -42,6 +42,7 @@ struct ScanLists {
   uint32_t* keys = nullptr;    // [T][kListM][scan_grid] order keys
   uint32_t* idx = nullptr;     // [T][kListM][scan_grid] key indices
   uint32_t* count = nullptr;   // [T][scan_grid] kept | (more than kListM visible) << 31
+  bool store_scores = true;    // also write the scores (else the selection recomputes them if it must)
 };
 int scan_grid(int64_t Lk);     // workgroups of the decode scan
 int scan_list_cap(int64_t Lk); // keys a workgroup of the scan without lists scores per row (at most)
@@ -100,6 +101,10 @@ struct DecodeArgs {
   AttnArgs a;                  // q, k, v, n_rows = Lk, T, sink, sm_scale, out, lse
   const float* scores;         // [T][ld] (re-selection when the lists may miss a winner)
   int64_t ld;
+  float* rescore;              // null, or [T][ld]: the scan stored no scores, the re-selection recomputes them here
+  const uint8_t* q_idx;        // the scan's inputs, for the recomputation
+  const float* w;
+  const uint8_t* k_idx;
   int64_t Lk;
   int k;
   const uint32_t* lkeys;       // scan lists (ScanLists layout)

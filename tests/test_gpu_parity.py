@@ -303,16 +303,26 @@ def test_swa_attention(dev, window):
 
 # ------------------------------------------------------------ fused decode step
 
-def run_decode(dev, d, Lk, T, k, ws=None, sink=True):
+def run_decode(dev, d, Lk, T, k, ws=None, sink=True, with_scores=True):
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    scores = torch.empty((T, Lk), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, Lk), dtype=torch.float32, device=dev) if with_scores else None
     lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
     out = binding.dsa_decode_step(g(d["q_idx"], dev), g(d["w"], dev), g(d["k_idx"], dev), g(d["q"], dev),
                                   g(d["k"], dev), g(d["v"], dev), Lk, T, k,
                                   g(d["sink"], dev) if sink else None, float(d["sm_scale"]),
                                   lse=lse, idx_out=idx, scores_out=scores, ws=ws)
     torch.cuda.synchronize()
-    return out.float().cpu().numpy(), idx.cpu().numpy(), scores.cpu().numpy(), lse.cpu().numpy()
+    return (out.float().cpu().numpy(), idx.cpu().numpy(), scores.cpu().numpy() if with_scores else None,
+            lse.cpu().numpy())
+
+
+def check_same_without_scores(dev, d, Lk, T, k, o, idx, lse):
+    # without scores_out the scan stores no scores and a re-selection
+    # recomputes them: every output must be the same bits
+    o2, idx2, _, lse2 = run_decode(dev, d, Lk, T, k, with_scores=False)
+    assert np.array_equal(idx2, idx)
+    assert np.array_equal(o2.view(np.uint32), o.view(np.uint32))
+    assert np.array_equal(lse2.view(np.uint32), lse.view(np.uint32))
 
 
 def check_decode(d, Lk, T, k, o, idx, S, sink=True):
@@ -335,8 +345,10 @@ def check_decode(d, Lk, T, k, o, idx, S, sink=True):
 def test_decode_step(dev, L, T, k, sink):
     cfg = synth.DecodeConfig("t", L=L, T=T, k=k, plant_frac=0.01, seed=L + T)
     d = synth.decode_inputs(cfg)
-    o, idx, S, _ = run_decode(dev, d, cfg.Lk, T, k, sink=sink)
+    o, idx, S, lse = run_decode(dev, d, cfg.Lk, T, k, sink=sink)
     check_decode(d, cfg.Lk, T, k, o, idx, S, sink=sink)
+    if sink:
+        check_same_without_scores(dev, d, cfg.Lk, T, k, o, idx, lse)
 
 
 def test_decode_step_deterministic_and_workspace_reuse(dev):
@@ -378,8 +390,41 @@ def clustered_inputs(L, T, c0, c1, seed):
                                        (300000, 1, 299000, 300001)])
 def test_decode_step_clustered_winners(dev, L, T, c0, c1):
     d, Lk = clustered_inputs(L, T, c0, c1, seed=L + c0)
-    o, idx, S, _ = run_decode(dev, d, Lk, T, 2048)
+    o, idx, S, lse = run_decode(dev, d, Lk, T, 2048)
     check_decode(d, Lk, T, 2048, o, idx, S)
+    check_same_without_scores(dev, d, Lk, T, 2048, o, idx, lse)
+
+
+@pytest.mark.parametrize("L,T", [(100000, 1), (100000, 2), (300000, 1)])
+def test_decode_step_overfull_list(dev, L, T):
+    # The scan deals 16-key tiles round-robin to its G workgroups (G = min(512,
+    # key groups of 256)), so tiles w0, w0 + G, w0 + 2G, w0 + 3G all feed
+    # workgroup w0's list: 64 near-best keys there overfill its 32 entries and
+    # force the re-selection from the whole row (stored, or recomputed when
+    # no scores are requested).
+    cfg = synth.DecodeConfig("o", L=L, T=T, k=2048, plant_frac=0.0, seed=L + T)
+    d = synth.decode_inputs(cfg)
+    Lk = cfg.Lk
+    d["q_idx"] = np.repeat(d["q_idx"][:1], T, axis=0)         # every row favours the same keys
+    d["w"] = np.repeat(d["w"][:1], T, axis=0)
+    G = min(512, -(-(-(-Lk // 16)) // 16))
+    S = oracle.index_scores(d["q_idx"], d["w"], d["k_idx"], Lk, T)
+    best_row = d["k_idx"][int(np.argmax(S[0, :Lk - T + 1]))].copy()
+    rng = np.random.default_rng(L)
+    w0 = 7
+    d["k_idx"] = d["k_idx"].copy()
+    for j in range(4):
+        tile = w0 + G * j
+        rows = np.repeat(best_row[None], 16, axis=0)
+        flip = rng.integers(0, 2, size=rows.shape).astype(np.uint8)
+        flip[(rows & 0x7F) >= 0x7E] = 0
+        d["k_idx"][16 * tile:16 * tile + 16] = rows ^ flip
+    o, idx, S, lse = run_decode(dev, d, Lk, T, 2048)
+    for t in range(T):
+        assert sum(int(np.sum((idx[t] >= 16 * (w0 + G * j)) & (idx[t] < 16 * (w0 + G * j) + 16)))
+                   for j in range(4)) > 32, "the planted keys did not overfill the list"
+    check_decode(d, Lk, T, 2048, o, idx, S)
+    check_same_without_scores(dev, d, Lk, T, 2048, o, idx, lse)
 
 
 @pytest.mark.parametrize("L,T,k", [(20000, 2, 2048), (70000, 1, 1000), (2500, 3, 2048)])
@@ -387,7 +432,8 @@ def test_decode_step_all_scores_tie(dev, L, T, k):
     cfg = synth.DecodeConfig("z", L=L, T=T, k=k, plant_frac=0.0, seed=L)
     d = synth.decode_inputs(cfg)
     d["q_idx"] = np.zeros_like(d["q_idx"])          # every score is zero
-    o, idx, S, _ = run_decode(dev, d, cfg.Lk, T, k)
+    o, idx, S, lse = run_decode(dev, d, cfg.Lk, T, k)
+    check_same_without_scores(dev, d, cfg.Lk, T, k, o, idx, lse)
     assert np.all(S[:, :cfg.Lk - T + 1] == 0)
     for t in range(T):
         n = min(k, cfg.Lk - T + t + 1)
