@@ -85,7 +85,8 @@ static_assert(sizeof(ListShared<4>) == 8 * 4 * 4 * kBufCap + 4 * 4 * kListM, "li
 
 // Cuts a wave's buffer (n entries, n <= kBufCap) back to its top kListM by
 // (key desc, index asc), in place and in no particular order; returns the
-// new count and sets *theta to the smallest key kept when the buffer was cut.
+// new count and sets *theta, when the buffer was cut, to a key at or below the
+// smallest one kept and at or above every key dropped.
 // The kListM-th key and, for ties, the kept indices are found bit by bit with
 // ballots over the E entries each lane holds (n <= 64 E).
 template <int E>
@@ -106,11 +107,29 @@ __device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, u
     for (int q = 0; q < E; ++q) c += (uint32_t)__popcll(__ballot(v[q] && kk[q] >= x));
     return c;
   };
-  uint32_t tau = 0;
+  // The candidates lie in [lo, hi], so the bits above the highest one in
+  // which lo and hi differ are common to all and need no test.  The descent
+  // finds the largest tau with at least kListM keys >= tau, and stops early at
+  // a tau with exactly kListM (those keys are then the top kListM, and tau a
+  // valid threshold: no key below it can enter).
+  uint32_t hl = 0u, ll = 0xFFFFFFFFu;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int q = 0; q < E; ++q)
+    if (v[q]) {
+      hl = hl > kk[q] ? hl : kk[q];
+      ll = ll < kk[q] ? ll : kk[q];
+    }
+  const uint32_t hi = __builtin_amdgcn_readlane(wave_incl_minmax<true>(hl), 63);
+  const uint32_t lo = __builtin_amdgcn_readlane(wave_incl_minmax<false>(ll), 63);
+  const uint32_t diff = hi ^ lo;
+  uint32_t tau = diff ? hi & ~(0xFFFFFFFFu >> __builtin_clz(diff)) : hi;
+  for (int bit = diff ? 31 - __builtin_clz(diff) : -1; bit >= 0; --bit) {
     const uint32_t tr = tau | (1u << bit);
-    if (count_ge(tr) >= (uint32_t)kListM) tau = tr;
+    const uint32_t c = count_ge(tr);
+    if (c >= (uint32_t)kListM) {
+      tau = tr;
+      if (c == (uint32_t)kListM) break;
+    }
   }
   const uint32_t above = tau == 0xFFFFFFFFu ? 0u : count_ge(tau + 1u);
   const uint32_t r = (uint32_t)kListM - above;             // tau-equal entries to keep
