@@ -199,6 +199,9 @@ dsa_status swa_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* 
  * ([NoFA] Figure 1, the order of one DSA module).  Arguments are those of the
  * three calls above; idx_out ([T][k] int32) optionally receives the selected
  * set; scores_out ([T][ld_scores] float32) optionally receives the scores.
+ * Without scores_out the step may store no scores at all (the results are the
+ * same; only a rare slow re-selection then recomputes them in ws), so asking
+ * for them costs time.
  * Limits: 1 <= T <= 8, 1 <= k <= 2048.  Needs ws (DSA_OP_DECODE_STEP).
  */
 dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
