@@ -190,6 +190,7 @@ def topk_ref_exact(S, Lk, T, k):
     (4, 131076, 2048, "planted"), (1, 131076, 2048, "wide"), (8, 4096, 512, "normal"),
     (17, 5000, 2048, "normal"), (40, 33000, 2048, "ties"), (20, 3000, 2048, "allequal"),
     (24, 20000, 64, "planted"), (32, 100, 2048, "normal"),
+    (3, 16386, 1000, "ties"), (1, 16384, 2048, "allequal"), (2, 16385, 2048, "negative"),
 ])
 def test_topk_bit_exact(dev, T, Lk, k, kind):
     rng = np.random.default_rng(zlib.crc32(repr((T, Lk, k, kind)).encode()))
