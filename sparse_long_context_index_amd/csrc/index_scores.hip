@@ -430,8 +430,10 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 }  // namespace
 
 int scan_grid(int64_t Lk) {
-  const int64_t ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
-  return (int)(ngroups < kScanBlocks ? ngroups : kScanBlocks);
+  // one list per workgroup and up to one workgroup per 16-key tile: a short
+  // row still spreads over many lists (an 8K-key row over 512)
+  const int64_t ntiles = cdiv(Lk, 16);
+  return (int)(ntiles < kScanBlocks ? ntiles : kScanBlocks);
 }
 
 // the scan without lists streams groups of 16 consecutive tiles with 3

@@ -430,6 +430,48 @@ struct RowCand {
 constexpr int kSmallRow = 16384;                   // rows up to this many keys stay in LDS
 static_assert(kSmallRow % kRowThreads == 0 && kSmallRow / 32 <= DSA_TOPK_MAX, "short-row layout");
 
+// The top-k of a short row (k < n <= kSmallRow): its order keys are read once
+// into K (LDS) and the three-digit radix descent runs there (ties: a descent
+// over the complemented indices); the kept set leaves in index order through
+// the bitmap bm (n / 32 words).  All NT threads call it; scan_sm holds NT / 64
+// words.
+template <int NT>
+__device__ void short_row_select(const float* __restrict__ row, int n, int k, uint32_t* K, RadixShared& rs,
+                                 uint32_t* bm, uint32_t* scan_sm, int32_t* out_row) {
+  constexpr int kS = kSmallRow / NT;
+  float v[kS];
+#pragma unroll
+  for (int e = 0; e < kS; ++e) {
+    if (e % 8 == 0 && e * NT >= n) break;
+    const int s = e * NT + (int)threadIdx.x;
+    v[e] = row[s < n ? s : n - 1];
+  }
+#pragma unroll
+  for (int e = 0; e < kS; ++e) {
+    if (e % 8 == 0 && e * NT >= n) break;
+    const int s = e * NT + (int)threadIdx.x;
+    if (s < n) K[s] = order_key(v[e]);
+  }
+  __syncthreads();
+  uint32_t tau, r, eq;
+  radix_threshold<NT>([&](int i) { return K[i]; }, n, (uint32_t)k, rs, &tau, &r, &eq);
+  uint32_t imax = 0xFFFFFFFFu;
+  if (eq > r) {                                        // block-uniform
+    uint32_t tau2, r2, eq2;
+    radix_threshold<NT>([&](int i) { return K[i] == tau ? ~(uint32_t)i : 0u; }, n, r, rs, &tau2, &r2, &eq2);
+    imax = ~tau2;
+  }
+  const int nw = (n + 31) / 32;
+  for (int i = threadIdx.x; i < nw; i += NT) bm[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t key = K[i];
+    if (key > tau || (key == tau && (uint32_t)i <= imax)) atomicOr(&bm[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  bitmap_emit<NT>(bm, nw, scan_sm, k, out_row);
+}
+
 union RowShared {
   uint32_t rep[kRowReps * kRepStride];
   static_assert(kRowReps * kRepStride >= kSmallRow, "a short row's keys fit the level-1 copies' space");
@@ -464,43 +506,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     // every visible key is kept
     for (int j = threadIdx.x; j < k; j += kRowThreads) out_row[j] = j < n ? j : -1;
   } else if (n <= (int64_t)kSmallRow) {
-    // A short row: its order keys are read once into LDS and the three-digit
-    // radix descent runs there (ties: a descent over the complemented
-    // indices); the kept set leaves in index order through a bitmap.
-    uint32_t* K = rsh.rep;
-    constexpr int kS = kSmallRow / kRowThreads;
-    float v[kS];
-#pragma unroll
-    for (int e = 0; e < kS; ++e) {
-      if (e % 8 == 0 && (int64_t)e * kRowThreads >= n) break;
-      const int s = e * kRowThreads + threadIdx.x;
-      v[e] = row[s < n ? s : n - 1];
-    }
-#pragma unroll
-    for (int e = 0; e < kS; ++e) {
-      if (e % 8 == 0 && (int64_t)e * kRowThreads >= n) break;
-      const int s = e * kRowThreads + threadIdx.x;
-      if (s < n) K[s] = order_key(v[e]);
-    }
-    __syncthreads();
-    uint32_t tau, r, eq;
-    radix_threshold<kRowThreads>([&](int i) { return K[i]; }, (int)n, (uint32_t)k, sh.rs, &tau, &r, &eq);
-    uint32_t imax = 0xFFFFFFFFu;
-    if (eq > r) {                                      // block-uniform
-      uint32_t tau2, r2, eq2;
-      radix_threshold<kRowThreads>([&](int i) { return K[i] == tau ? ~(uint32_t)i : 0u; }, (int)n, r, sh.rs,
-                                   &tau2, &r2, &eq2);
-      imax = ~tau2;
-    }
-    const int nw = (int)((n + 31) / 32);
-    for (int i = threadIdx.x; i < nw; i += kRowThreads) sh.sel[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < (int)n; i += kRowThreads) {
-      const uint32_t key = K[i];
-      if (key > tau || (key == tau && (uint32_t)i <= imax)) atomicOr(&sh.sel[i >> 5], 1u << (i & 31));
-    }
-    __syncthreads();
-    bitmap_emit<kRowThreads>(sh.sel, nw, fs.scan, k, out_row);
+    short_row_select<kRowThreads>(row, (int)n, k, rsh.rep, sh.rs, sh.sel, fs.scan, out_row);
   } else {
     // ---- level-1 histogram
     static_assert((kRowReps * kRepStride) % 4 == 0, "16-byte clears");
