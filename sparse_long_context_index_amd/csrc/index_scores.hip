@@ -78,10 +78,10 @@ template <int T>
 struct ListShared {
   alignas(16) uint32_t bk[4][T][kBufCap];          // wave buffers: order keys
   alignas(16) uint32_t bi[4][T][kBufCap];          // and key indices
-  uint32_t rank[4 * kListM];                       // merge: partial ranks of the wave sets' entries
+  uint32_t rank[T][4 * kListM];                    // merge: partial ranks of the wave sets' entries
 };
 static_assert(sizeof(ListShared<1>) == 8 * 4 * kBufCap + 4 * 4 * kListM, "list LDS size");
-static_assert(sizeof(ListShared<4>) == 8 * 4 * 4 * kBufCap + 4 * 4 * kListM, "list LDS size");
+static_assert(sizeof(ListShared<4>) == 4 * (8 * 4 * kBufCap + 4 * 4 * kListM), "list LDS size");
 
 // Cuts a wave's buffer (n entries, n <= kBufCap) back to its top kListM by
 // (key desc, index asc), in place and in no particular order; returns the
@@ -89,18 +89,12 @@ static_assert(sizeof(ListShared<4>) == 8 * 4 * 4 * kBufCap + 4 * 4 * kListM, "li
 // smallest one kept and at or above every key dropped.
 // The kListM-th key and, for ties, the kept indices are found bit by bit with
 // ballots over the E entries each lane holds (n <= 64 E).
+// The top kListM by (key desc, index asc) of the valid entries (v) that the
+// wave's lanes hold, E each, when more than kListM are valid: sets keep[] and
+// *theta (see wave_cut_top_e).
 template <int E>
-__device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, uint32_t n, uint32_t* theta) {
-  const int lane = threadIdx.x & 63;
-  bool v[E];
-  uint32_t kk[E], ii[E];
-#pragma unroll
-  for (int q = 0; q < E; ++q) {
-    v[q] = (uint32_t)(lane + 64 * q) < n;
-    kk[q] = bk[lane + 64 * q];
-    ii[q] = bi[lane + 64 * q];
-    if (!v[q]) kk[q] = 0u;
-  }
+__device__ __forceinline__ void wave_top_keep(const uint32_t* kk, const uint32_t* ii, const bool* v, bool* keep,
+                                              uint32_t* theta) {
   auto count_ge = [&](uint32_t x) {
     uint32_t c = 0;
 #pragma unroll
@@ -149,13 +143,29 @@ __device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, u
     }
     imax = ~y;
   }
+#pragma unroll
+  for (int q = 0; q < E; ++q) keep[q] = v[q] && (kk[q] > tau || (kk[q] == tau && ii[q] <= imax));
+  *theta = tau;
+}
+
+template <int E>
+__device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, uint32_t n, uint32_t* theta) {
+  const int lane = threadIdx.x & 63;
+  bool v[E], keep[E];
+  uint32_t kk[E], ii[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    v[q] = (uint32_t)(lane + 64 * q) < n;
+    kk[q] = bk[lane + 64 * q];
+    ii[q] = bi[lane + 64 * q];
+    if (!v[q]) kk[q] = 0u;
+  }
+  wave_top_keep<E>(kk, ii, v, keep, theta);
   const uint64_t below = (1ull << lane) - 1ull;
-  bool keep[E];
   uint32_t pos[E];
   uint32_t base = 0;
 #pragma unroll
   for (int q = 0; q < E; ++q) {
-    keep[q] = v[q] && (kk[q] > tau || (kk[q] == tau && ii[q] <= imax));
     const uint64_t m = __ballot(keep[q]);
     pos[q] = base + (uint32_t)__popcll(m & below);
     base += (uint32_t)__popcll(m);
@@ -171,7 +181,6 @@ __device__ __forceinline__ uint32_t wave_cut_top_e(uint32_t* bk, uint32_t* bi, u
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  *theta = tau;
   return (uint32_t)kListM;
 }
 
@@ -391,10 +400,47 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       }
     }
     __syncthreads();
+    // Wave w merges rows w, w + 4, ...: the row's top kListM of the four wave
+    // sets (128 entries, two per lane, key 0 = empty), compacted into the
+    // row's merge area, then each kept entry's rank among them (its place in
+    // the list, sorted by key desc, index asc).
     const uint32_t bx = blockIdx.x, G32 = gridDim.x;
-    const int e = threadIdx.x & (4 * kListM - 1);                // entry: wave e / kListM, slot e % kListM
-    const int half = threadIdx.x / (4 * kListM);                 // compares against waves 2 half, 2 half + 1
-    for (int t = 0; t < T; ++t) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int t = wave; t < T; t += 4) {                          // wave-uniform
+      uint32_t kk[2], ii[2];
+      bool v[2], keep[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        kk[q] = ls.bk[2 * q + (lane >> 5)][t][lane & 31];
+        ii[q] = ls.bi[2 * q + (lane >> 5)][t][lane & 31];
+        v[q] = kk[q] != 0u;
+        keep[q] = v[q];
+      }
+      const uint32_t nv = (uint32_t)__popcll(__ballot(v[0])) + (uint32_t)__popcll(__ballot(v[1]));
+      if (nv > (uint32_t)kListM) {
+        uint32_t th;
+        wave_top_keep<2>(kk, ii, v, keep, &th);
+      }
+      uint32_t* mk = ls.rank[t];                                 // kListM keys, then kListM indices
+      uint32_t* mi = ls.rank[t] + kListM;
+      const uint64_t m0 = __ballot(keep[0]), m1 = __ballot(keep[1]);
+      const uint32_t nk = (uint32_t)__popcll(m0) + (uint32_t)__popcll(m1);
+      const uint32_t pos0 = (uint32_t)__popcll(m0 & below), pos1 = (uint32_t)__popcll(m0) + (uint32_t)__popcll(m1 & below);
+      if (keep[0]) {
+        mk[pos0] = kk[0];
+        mi[pos0] = ii[0];
+      }
+      if (keep[1]) {
+        mk[pos1] = kk[1];
+        mi[pos1] = ii[1];
+      }
+      if ((uint32_t)lane >= nk && lane < kListM) {             // padding ranks below every key
+        mk[lane] = 0u;
+        mi[lane] = 0xFFFFFFFFu;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const uint32_t P = (uint32_t)(Lk - T + t + 1);            // keys visible to row t
       // visible keys of this workgroup: whole tiles below P / 16, plus the partial one
       const uint32_t F = P >> 4, rem = P & 15u;
@@ -402,27 +448,19 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       if (rem && F >= bx && (F - bx) % G32 == 0) n_vis += rem;
       const bool full = n_vis > (uint32_t)kListM;
       const uint32_t kept = full ? (uint32_t)kListM : n_vis;
-      // merge: the rank of an entry among the 4 kListM entries is the number preceding it
-      const uint32_t key = ls.bk[e / kListM][t][e % kListM], id = ls.bi[e / kListM][t][e % kListM];
-      const uint32_t part = count_preceding<kListM>(ls.bk[2 * half][t], ls.bi[2 * half][t], key, id) +
-                            count_preceding<kListM>(ls.bk[2 * half + 1][t], ls.bi[2 * half + 1][t], key, id);
-      if (half == 1) ls.rank[e] = part;
-      __syncthreads();
-      if (half == 0 && key != 0u) {
-        const uint32_t rank = part + ls.rank[e];
-        if (rank < (uint32_t)kListM) {
-          const size_t off = ((size_t)t * kListM + rank) * G32 + bx;
-          lists.keys[off] = key;
-          lists.idx[off] = id;
-        }
+      if ((uint32_t)lane < nk) {
+        const uint32_t key = mk[lane], id = mi[lane];
+        const uint32_t rank = count_preceding<kListM>(mk, mi, key, id);
+        const size_t off = ((size_t)t * kListM + rank) * G32 + bx;
+        lists.keys[off] = key;
+        lists.idx[off] = id;
       }
-      if (threadIdx.x >= kept && threadIdx.x < kListM) {         // unused entries
-        const size_t off = ((size_t)t * kListM + threadIdx.x) * G32 + bx;
+      if ((uint32_t)lane >= kept && lane < kListM) {             // unused entries
+        const size_t off = ((size_t)t * kListM + lane) * G32 + bx;
         lists.keys[off] = 0u;
         lists.idx[off] = 0xFFFFFFFFu;
       }
-      if (threadIdx.x == 0) lists.count[(size_t)t * G32 + bx] = kept | (full ? 0x80000000u : 0u);
-      __syncthreads();
+      if (lane == 0) lists.count[(size_t)t * G32 + bx] = kept | (full ? 0x80000000u : 0u);
     }
   }
 }
@@ -451,7 +489,7 @@ int scan_list_cap(int64_t Lk) {
 size_t scan_lds_bytes(int64_t Lk, int T, bool lists) {
   (void)Lk;
   return (size_t)4 * kScanUnroll * 16 * kStageRow +
-         (lists ? (size_t)8 * 4 * T * kBufCap + sizeof(uint32_t) * 4 * kListM : 0);
+         (lists ? (size_t)T * (8 * 4 * kBufCap + sizeof(uint32_t) * 4 * kListM) : 0);
 }
 
 hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
