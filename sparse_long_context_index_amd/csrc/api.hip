@@ -87,28 +87,33 @@ DecodeLayout decode_layout(int64_t Lk, int T, int k) {
 
 // workspace of the fused prefill top-k
 struct PrefillLayout {
-  size_t sample, theta, count, failed, cand, fb, topk, total;
-  int64_t ld_sample;
+  size_t sample, theta, cw, tnorm, count, failed, cand, fb, total;
+  int64_t ld_sample, ld_fb;
+  int fb_blocks;
 };
 
 PrefillLayout prefill_layout(int64_t Lk, int T) {
   PrefillLayout d;
   d.ld_sample = (cdiv(Lk, kPrefillStep) + 3) / 4 * 4;
-  size_t off = kCounterRegionBytes;            // the fallback top-k's counters
+  d.ld_fb = (Lk + 63) / 64 * 64;
+  d.fb_blocks = T < kPrefillFallbackBlocks ? T : kPrefillFallbackBlocks;
+  size_t off = kCounterRegionBytes;
   d.sample = off;
   off += align_up((size_t)T * d.ld_sample * sizeof(float));
   d.theta = off;
   off += align_up((size_t)T * sizeof(uint32_t));
+  d.cw = off;
+  off += align_up((size_t)T * sizeof(float));
+  d.tnorm = off;
+  off += align_up((size_t)cdiv(Lk, kPrefillTileKeys) * sizeof(float));
   d.count = off;                               // T row counters, then the failure count
   off += align_up(((size_t)T + 4) * sizeof(uint32_t));
   d.failed = off;
   off += align_up((size_t)T * sizeof(uint32_t));
   d.cand = off;
   off += align_up((size_t)T * kPrefillCap * sizeof(uint2));
-  d.fb = off;
-  off += align_up((size_t)Lk * sizeof(float));
-  d.topk = off;
-  off += align_up(topk_scratch_bytes(Lk, 1, DSA_TOPK_MAX));
+  d.fb = off;                                  // score rows of the exact fallback
+  off += align_up((size_t)d.fb_blocks * d.ld_fb * sizeof(float));
   d.total = off;
   return d;
 }
@@ -462,35 +467,24 @@ dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t*
   uint32_t* count = reinterpret_cast<uint32_t*>(base + d.count);
   uint32_t* nfail = count + T;
   uint32_t* failed = reinterpret_cast<uint32_t*>(base + d.failed);
-  const PrefillCand pc{theta, count, reinterpret_cast<uint2*>(base + d.cand), kPrefillCap};
+  PrefillCand pc{theta, count, reinterpret_cast<uint2*>(base + d.cand), kPrefillCap};
+  pc.cw = reinterpret_cast<float*>(base + d.cw);
+  pc.tnorm = reinterpret_cast<float*>(base + d.tnorm);
   hipError_t e = launch_zero(count, align_up(((size_t)T + 4) * sizeof(uint32_t)), st);
+  if (e == hipSuccess) e = launch_key_tile_norms(k_idx, Lk, const_cast<float*>(pc.tnorm), st);
   if (e == hipSuccess) e = launch_idx_gemm_sample(q_idx, w, k_idx, Lk, T, kPrefillStep, sample, d.ld_sample, st);
-  if (e == hipSuccess) e = launch_prefill_theta(sample, d.ld_sample, Lk, T, kPrefillStep, k, kPrefillCap, theta, st);
+  if (e == hipSuccess)
+    e = launch_prefill_theta(sample, d.ld_sample, q_idx, w, Lk, T, kPrefillStep, k, kPrefillCap, theta,
+                             const_cast<float*>(pc.cw), st);
   if (e == hipSuccess) e = launch_idx_gemm_cand(q_idx, w, k_idx, Lk, T, pc, st);
+  if (e == hipSuccess) e = launch_prefill_rescore(pc, q_idx, w, k_idx, T, st);
   if (e == hipSuccess) e = launch_prefill_refine(pc, Lk, T, k, idx, nfail, failed, st);
-  if (e != hipSuccess) return DSA_ERR_HIP;
-  // rows whose candidates did not fit or were too few: recompute each with the
-  // same contraction over its visible keys and the row top-k
-  uint32_t nf = 0;
-  if (hipMemcpyAsync(&nf, nfail, sizeof(nf), hipMemcpyDeviceToHost, st) != hipSuccess) return DSA_ERR_HIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return DSA_ERR_HIP;
-  if (nf == 0) return DSA_OK;
-  if (nf > (uint32_t)T) return DSA_ERR_HIP;
-  std::vector<uint32_t> rows(nf);
-  if (hipMemcpyAsync(rows.data(), failed, nf * sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return DSA_ERR_HIP;
-  float* fb = reinterpret_cast<float*>(base + d.fb);
-  for (uint32_t t : rows) {
-    if (t >= (uint32_t)T) return DSA_ERR_HIP;
-    const int64_t nvis = Lk - T + t + 1;
-    e = launch_idx_gemm(q_idx + (size_t)t * DSA_IDX_HEADS * DSA_IDX_DIM, w + (size_t)t * DSA_IDX_HEADS, k_idx, nvis, 1,
-                        fb, nvis, st);
-    if (e == hipSuccess)
-      e = launch_topk(fb, nvis, nvis, 1, k, idx + (size_t)t * k, ws, base + d.topk, st);
-    if (e != hipSuccess) return DSA_ERR_HIP;
-  }
-  return DSA_OK;
+  // rows whose candidates did not fit or did not hold their top-k: recomputed
+  // exactly on the device (the launch ends at once when there are none)
+  if (e == hipSuccess)
+    e = launch_prefill_fallback(q_idx, w, k_idx, Lk, T, k, nfail, failed, reinterpret_cast<float*>(base + d.fb),
+                                d.ld_fb, d.fb_blocks, idx, st);
+  return hip_status(e);
 }
 
 }  // extern "C"

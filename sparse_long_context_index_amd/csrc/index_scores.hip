@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       __shared__ uint32_t deal_sm[4];
       __shared__ int64_t deal_out[3];
       int64_t f0;
-      const int64_t n_i = (int)threadIdx.x < sb.spread ? seq_keys(sb, threadIdx.x, &f0) : 0;
+      int64_t n_i = (int)threadIdx.x < sb.spread ? seq_keys(sb, threadIdx.x, &f0) - sb.tail : 0;
+      n_i = n_i > 0 ? n_i : 0;
       const uint32_t ng = (uint32_t)cdiv(cdiv(n_i, 16), 4 * kScanUnroll);
       uint32_t N, used;
       (void)block_excl_scan<256>(ng, deal_sm, &N);
@@ -257,11 +258,13 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       G = deal_out[2];
     }
     int64_t first;
-    Lk = seq_keys(sb, b, &first);
-    q_idx += (size_t)b * T * 16 * 128;
-    w += (size_t)b * T * 16;
+    Lk = seq_keys(sb, b, &first) - sb.tail;
+    Lk = Lk > 0 ? Lk : 0;
+    const int ts = sb.tstride ? sb.tstride : T;
+    q_idx += (size_t)b * ts * 16 * 128;
+    w += (size_t)b * ts * 16;
     k_idx += first * 128;
-    scores += (size_t)b * T * ld;
+    scores += (size_t)b * ts * ld;
     ngroups = cdiv(cdiv(Lk, 16), 4 * kScanUnroll);
     if (Lk == 0) return;
   }
@@ -533,7 +536,22 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
 hipError_t launch_index_scores_batch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const SeqBatch& sb,
                                      int B, int T, float* scores, int64_t ld, hipStream_t st) {
   if (B < 1 || T < 1 || ld < sb.max_len || B > 65535) return hipErrorInvalidValue;
-  if (T > kDecodeTMax) return launch_idx_gemm_batch(q_idx, w, k_idx, sb, B, T, scores, ld, st);
+  if (sb.tstride == 0 && T > kDecodeTMax) {
+    // more tokens than one scan holds: the scan over groups of up to
+    // kDecodeTMax tokens (the same exact arithmetic; the keys are read once
+    // per group)
+    for (int t0 = 0; t0 < T; t0 += kDecodeTMax) {
+      const int tg = T - t0 < kDecodeTMax ? T - t0 : kDecodeTMax;
+      SeqBatch g = sb;
+      g.tstride = T;
+      g.tail = T - t0 - tg;
+      const hipError_t e = launch_index_scores_batch(q_idx + (size_t)t0 * 16 * 128, w + (size_t)t0 * 16, k_idx, g, B,
+                                                     tg, scores + (size_t)t0 * ld, ld, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (T > kDecodeTMax) return hipErrorInvalidValue;
   const size_t lds = scan_lds_bytes(sb.max_len, T, false);
   const TopkCounters ctr{};
   const int64_t max_groups = cdiv(cdiv(sb.max_len, 16), 4 * kScanUnroll);

@@ -75,3 +75,66 @@ __device__ __forceinline__ float sum_rows4x4(float x0, float x1, float x2, float
 }
 
 }  // namespace dsa
+
+namespace dsa {
+
+// ---------------------------------------------------------------- exact scores
+// One query token's operands for the exact index arithmetic of the decode
+// scan: the 16 heads' fp8 bytes widened to bf16 (lane: head col, k-group grp)
+// and the weights of the 4 heads whose logits the lane's accumulator holds.
+struct ExactQuery {
+  bf16x8 a[4];
+  float wv[4];
+};
+
+__device__ __forceinline__ void load_exact_query(const uint8_t* q_t, const float* w_t, ExactQuery& eq) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  widen_fp8(load_frag32_cached(q_t + (size_t)col * 128 + 32 * grp), eq.a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eq.wv[i] = w_t[4 * grp + i];
+}
+
+// The score of the key whose 32 bytes of k-group (lane / 16) this lane holds
+// in kr (one key per lane column): fp8 widened to bf16 (lossless), four bf16
+// MFMAs over the 128 dims (exact products, fp32 sums), the ReLU-weighted head
+// sum.  Same operands in the same order as the decode scan, so the same bits;
+// every lane of the column receives the score.
+__device__ __forceinline__ float exact_score(const ExactQuery& eq, const i32x8& kr) {
+  bf16x8 b[4];
+  widen_fp8(kr, b);
+  f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) c = mfma_bf16_16x16x32(eq.a[k4], b[k4], c);
+  return relu_weighted_sum(c, eq.wv);
+}
+
+// Exact scores of query token q_t / w_t against keys 0 .. n - 1 into row,
+// by the NT threads of a workgroup (each wave takes 16-key tiles, U tiles'
+// loads in flight).  Plain stores: the caller synchronises before reading.
+template <int NT>
+__device__ __forceinline__ void exact_scores_block(const uint8_t* q_t, const float* w_t, const uint8_t* k_idx,
+                                                   int64_t n, float* row) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  ExactQuery eq;
+  load_exact_query(q_t, w_t, eq);
+  constexpr int U = 8;
+  const int64_t ntiles = cdiv(n, 16);
+  for (int64_t t0 = (int64_t)wave * U; t0 < ntiles; t0 += (int64_t)(NT / 64) * U) {
+    i32x8 kr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = (t0 + u) * 16 + col;
+      kr[u] = load_frag32_cached(k_idx + (key < n ? key : n - 1) * 128 + 32 * grp);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = (t0 + u) * 16 + col;
+      const float s = exact_score(eq, kr[u]);
+      if (grp == 0 && key < n) row[key] = s;
+    }
+  }
+}
+
+}  // namespace dsa

@@ -23,6 +23,12 @@ struct SeqBatch {
   int64_t n_rows = 0;
   int64_t max_len = 0;
   int32_t spread = 0;               // the batch scan: B when its workgroups are dealt by length (B <= 256)
+  // the batch scan over a group of a sequence's tokens: tstride tokens per
+  // sequence in the query, weight and score layouts (0: the launch's T), and
+  // `tail` more tokens after the group (its keys end tail rows before the
+  // sequence's last)
+  int32_t tstride = 0;
+  int32_t tail = 0;
 };
 
 // keys of sequence b (0 when its descriptor is invalid); *first receives its first row
@@ -130,11 +136,19 @@ hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const ui
 // candidate emission: every visible key whose order key reaches theta[t] is
 // appended to row t's slots as (order key, index); count[t] counts them all
 // (slots past cap are not written)
+// A key is a candidate of row t when the contraction's score reaches theta[t]
+// lowered by cw[t] * tnorm[tile]: cw[t] bounds, per unit of key norm, how far
+// the contraction's score of row t can lie from the exact one (see the fused
+// prefill top-k), tnorm[tile] is the largest key norm of the key's
+// kPrefillTileKeys-key tile.
+constexpr int kPrefillTileKeys = 2048;
 struct PrefillCand {
   const uint32_t* theta;   // [T]
   uint32_t* count;         // [T], zero before the launch
   uint2* cand;             // [T][cap]
   int cap;
+  const float* cw = nullptr;     // [T]
+  const float* tnorm = nullptr;  // [ceil(Lk / kPrefillTileKeys)]
 };
 hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                                 const PrefillCand& pc, hipStream_t st);
@@ -142,14 +156,29 @@ hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint
 // ---- fused prefill top-k (prefill_topk.hip)
 constexpr int kPrefillStep = 64;           // key sample stride of the threshold estimate
 constexpr int kPrefillCap = 8192;          // candidate slots per row
+constexpr int kPrefillFallbackBlocks = 64; // workgroups (and score rows of workspace) of the exact fallback
 size_t prefill_refine_lds(int cap);
-// theta[t]: order key of the row's threshold (0: every visible key)
-hipError_t launch_prefill_theta(const float* sample, int64_t ld, int64_t Lk, int T, int step, int k, int cap,
-                                uint32_t* theta, hipStream_t st);
+// tnorm[j]: an upper bound of the largest Euclidean norm of keys
+// j * kPrefillTileKeys .. (j + 1) * kPrefillTileKeys - 1 (below Lk)
+hipError_t launch_key_tile_norms(const uint8_t* k_idx, int64_t Lk, float* tnorm, hipStream_t st);
+// theta[t]: order key of the row's threshold (0: every visible key); cw[t]:
+// the row's error factor (sum_h |w[t,h]| |q_idx[t,h]| times the relative
+// error bound of the contraction, rounded up)
+hipError_t launch_prefill_theta(const float* sample, int64_t ld, const uint8_t* q_idx, const float* w, int64_t Lk,
+                                int T, int step, int k, int cap, uint32_t* theta, float* cw, hipStream_t st);
+// the candidates' order keys recomputed with the exact index arithmetic (in place)
+hipError_t launch_prefill_rescore(const PrefillCand& pc, const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                                  int T, hipStream_t st);
 // exact top-k of each row from its candidates into idx [T][k]; rows whose
-// candidates do not fit or are too few are appended to failed (nfail counts)
+// candidates do not fit, or of which fewer than min(k, visible) reach the
+// row's threshold, are appended to failed (nfail counts)
 hipError_t launch_prefill_refine(const PrefillCand& pc, int64_t Lk, int T, int k, int32_t* idx, uint32_t* nfail,
                                  uint32_t* failed, hipStream_t st);
+// the listed rows (failed[0 .. *nfail)) recomputed exactly: scores of every
+// visible key into buf ([blocks][ld] floats), then the row top-k (topk.hip)
+hipError_t launch_prefill_fallback(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
+                                   int k, const uint32_t* nfail, const uint32_t* failed, float* buf, int64_t ld,
+                                   int blocks, int32_t* idx, hipStream_t st);
 
 // ---- index-selection recall (recall.hip)
 int recall_chunks(int64_t Lk);

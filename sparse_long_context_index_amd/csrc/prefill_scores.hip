@@ -24,7 +24,7 @@ namespace dsa {
 namespace {
 
 constexpr int kGemmTok = 32;     // tokens per workgroup (8 per wave)
-constexpr int kGemmKeys = 2048;  // keys per workgroup (128 blocks of 16)
+constexpr int kGemmKeys = kPrefillTileKeys;  // keys per workgroup (128 blocks of 16)
 constexpr int kGemmPF = 4;       // key blocks in flight per wave
 constexpr int kGemmGroupT = 32;  // token tiles per L2 super-tile
 
@@ -147,9 +147,23 @@ __device__ __forceinline__ float order_key_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// The candidate test of a row against a key tile: the row's threshold lowered
+// by the largest difference between this contraction's score and the exact
+// one that any key of the tile can show (cw = the row's error factor, tn = the
+// tile's largest key norm), formed in double and rounded down, never below
+// the lowest finite float (so a masked key, scored -inf, never passes).
+__device__ __forceinline__ float lowered_threshold(uint32_t theta, float cw, float tn) {
+  constexpr float kLowest = -3.402823466e38f;
+  if (theta == 0u) return kLowest;
+  const float f = __double2float_rd((double)order_key_to_float(theta) - (double)cw * (double)tn);
+  return f > kLowest ? f : kLowest;
+}
+
 enum GemmMode { kGemmScores = 0, kGemmSample = 1, kGemmCand = 2 };
 
 struct GemmArgs {
+  const float* cw;     // candidate mode: [T] per-row error factor (see PrefillCand)
+  const float* tnorm;  // candidate mode: [key tiles] largest key norm of each 2048-key tile
   const uint8_t* q_idx;
   const float* w;
   const uint8_t* k_idx;
@@ -241,8 +255,9 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
   __shared__ uint2 lcand[kMode == kGemmCand ? 4 : 1][kMode == kGemmCand ? 8 * kLocalCand : 1];
   __shared__ uint32_t lcnt[kMode == kGemmCand ? 4 : 1][8];
   if (kMode == kGemmCand) {
-    if (t0 + grp < T) th0 = order_key_to_float(ga.cand.theta[t0 + grp]);
-    if (t0 + grp + 4 < T) th1 = order_key_to_float(ga.cand.theta[t0 + grp + 4]);
+    const float tn = ga.tnorm[ktile];
+    if (t0 + grp < T) th0 = lowered_threshold(ga.cand.theta[t0 + grp], ga.cw[t0 + grp], tn);
+    if (t0 + grp + 4 < T) th1 = lowered_threshold(ga.cand.theta[t0 + grp + 4], ga.cw[t0 + grp + 4], tn);
   }
 #pragma unroll 1
   for (int kb = 0; kb < NB; kb += kGemmPF) {
@@ -340,9 +355,11 @@ hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const ui
 
 hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                                 const PrefillCand& pc, hipStream_t st) {
-  if (pc.cap < 1 || !pc.theta || !pc.count || !pc.cand) return hipErrorInvalidValue;
+  if (pc.cap < 1 || !pc.theta || !pc.count || !pc.cand || !pc.cw || !pc.tnorm) return hipErrorInvalidValue;
   GemmArgs ga = gemm_args(q_idx, w, k_idx, Lk, T, 1);
   ga.cand = pc;
+  ga.cw = pc.cw;
+  ga.tnorm = pc.tnorm;
   return launch_gemm<kGemmCand>(ga, st);
 }
 

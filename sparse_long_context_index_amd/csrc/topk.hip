@@ -27,6 +27,7 @@
 // A candidate slot that overflows switches the row's final pass to reading
 // the scores row itself (same result, slower).
 #include "dsa_common.hpp"
+#include "indexer.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -485,21 +486,10 @@ struct RowSel {
   uint32_t wcount[kRowWaves];
 };
 
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
-                                                               int64_t Lk, int T, int k,
-                                                               int32_t* __restrict__ idx, SeqBatch sb,
-                                                               int32_t* __restrict__ idx_rows) {
-  __shared__ __attribute__((aligned(16))) RowShared rsh;
-  __shared__ __attribute__((aligned(16))) RowSel sh;
-  __shared__ FinalShared fs;
-  const int t = blockIdx.x;
-  int64_t first = 0;
-  if (sb.len) Lk = seq_keys(sb, t / T, &first);        // batch: row t is token t % T of sequence t / T
-  const int tt = sb.len ? t % T : t;
-  int64_t n = Lk - T + tt + 1;
-  n = n > 0 ? n : 0;
-  const float* row = scores + (int64_t)t * ld;
-  int32_t* out_row = idx + (size_t)t * k;
+// The top-k of one scores row of n visible keys into out_row[0 .. k), by the
+// kRowThreads threads of a workgroup (the shared structures are the caller's).
+__device__ void row_topk(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out_row,
+                         RowShared& rsh, RowSel& sh, FinalShared& fs) {
   const int lane = threadIdx.x & 63;
 
   if (n <= (int64_t)k) {
@@ -647,6 +637,23 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       final_select<kRowThreads>(src, k, false, b1, (uint32_t)k - above1, h2, fs, out_row);
     }
   }
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t Lk, int T, int k,
+                                                               int32_t* __restrict__ idx, SeqBatch sb,
+                                                               int32_t* __restrict__ idx_rows) {
+  __shared__ __attribute__((aligned(16))) RowShared rsh;
+  __shared__ __attribute__((aligned(16))) RowSel sh;
+  __shared__ FinalShared fs;
+  const int t = blockIdx.x;
+  int64_t first = 0;
+  if (sb.len) Lk = seq_keys(sb, t / T, &first);        // batch: row t is token t % T of sequence t / T
+  const int tt = sb.len ? t % T : t;
+  int64_t n = Lk - T + tt + 1;
+  n = n > 0 ? n : 0;
+  int32_t* out_row = idx + (size_t)t * k;
+  row_topk(scores + (int64_t)t * ld, n, k, out_row, rsh, sh, fs);
   if (idx_rows) {
     // the same set as cache rows of the sequence
     __syncthreads();
@@ -654,6 +661,32 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       const int32_t v = out_row[j];
       idx_rows[(size_t)t * k + j] = v >= 0 ? (int32_t)(first + v) : -1;
     }
+  }
+}
+
+// The exact fallback of the fused prefill top-k: each workgroup takes the
+// listed rows blockIdx.x, blockIdx.x + gridDim.x, ... below *nfail, scores the
+// row's visible keys with the exact index arithmetic into its own buffer row
+// (buf + blockIdx.x * ld) and selects the row's top-k from it.  A launch with
+// no listed row ends at once.
+__global__ __launch_bounds__(kRowThreads) void prefill_fallback_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx, int64_t Lk,
+    int T, int k, const uint32_t* __restrict__ nfail, const uint32_t* __restrict__ failed, float* __restrict__ buf,
+    int64_t ld, int32_t* __restrict__ idx) {
+  __shared__ __attribute__((aligned(16))) RowShared rsh;
+  __shared__ __attribute__((aligned(16))) RowSel sh;
+  __shared__ FinalShared fs;
+  uint32_t nf = *nfail;
+  nf = nf < (uint32_t)T ? nf : (uint32_t)T;
+  float* row = buf + (int64_t)blockIdx.x * ld;
+  for (uint32_t i = blockIdx.x; i < nf; i += gridDim.x) {
+    const uint32_t t = failed[i];
+    if (t >= (uint32_t)T) continue;                    // block-uniform; never written so by the refine kernel
+    const int64_t n = Lk - T + (int64_t)t + 1;
+    exact_scores_block<kRowThreads>(q_idx + (size_t)t * 16 * 128, w + (size_t)t * 16, k_idx, n, row);
+    __syncthreads();
+    row_topk(row, n, k, idx + (size_t)t * k, rsh, sh, fs);
+    __syncthreads();
   }
 }
 
@@ -704,6 +737,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t Lk, int T, int k
 }
 
 bool topk_multi_block(int64_t Lk, int T, int k) { return multi_block(Lk, T, k); }
+
+hipError_t launch_prefill_fallback(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
+                                   int k, const uint32_t* nfail, const uint32_t* failed, float* buf, int64_t ld,
+                                   int blocks, int32_t* idx, hipStream_t st) {
+  if (blocks < 1 || ld < Lk || k < 1 || k > DSA_TOPK_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_fallback_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, q_idx, w, k_idx, Lk,
+                     T, k, nfail, failed, buf, ld, idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_batch(const float* scores, int64_t ld, const SeqBatch& sb, int B, int T, int k, int32_t* idx,
                              int32_t* idx_rows, hipStream_t st) {

@@ -342,6 +342,81 @@ def test_topk_check_detects_far_swap():
     assert not oracle.topk_check(ref[::-1].copy(), ref, S, 100)[0]   # not ascending
 
 
+def _scores_float32(q_idx, w, k_idx, order):
+    """Brute-force float32 evaluation of the index scores of one query token:
+    exact products (fp8 x fp8 fits float32), the 128-term dots summed in
+    float32 in the given dim order, ReLU, float32 products with w, the 16
+    heads summed in float32 -- every operation rounded by numpy's IEEE
+    float32 arithmetic."""
+    q = oracle.decode_e4m3(q_idx).astype(np.float32)          # [16,128], exact
+    k = oracle.decode_e4m3(k_idx).astype(np.float32)          # [n,128], exact
+    acc = np.zeros((k.shape[0], 16), np.float32)
+    for d in order:
+        acc = acc + (k[:, d:d + 1] * q[None, :, d])              # exact product, rounded sum
+    s = np.zeros(k.shape[0], np.float32)
+    for h in range(16):
+        s = s + np.float32(w[h]) * np.maximum(acc[:, h], np.float32(0))
+    return s.astype(np.float64)
+
+
+def test_score_error_bound_holds_for_float32_sums_in_any_order():
+    # brute force: the float32 scores in four summation orders stay within
+    # the bound of the exact scores, on full-range codes (incl. +-448 and
+    # subnormals) and on N(0,1) codes
+    rng = np.random.default_rng(21)
+    orders = [np.arange(128), np.arange(128)[::-1], rng.permutation(128),
+              np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])]
+    for draw in range(2):
+        if draw == 0:
+            q = rng.integers(0, 256, (1, 16, 128)).astype(np.uint8)
+            k = rng.integers(0, 256, (400, 128)).astype(np.uint8)
+            q[(q & 0x7F) == 0x7F] = 0x3F
+            k[(k & 0x7F) == 0x7F] = 0x3F
+        else:
+            q = synth.encode_e4m3(rng.standard_normal((1, 16, 128)).astype(np.float32))
+            k = synth.encode_e4m3(rng.standard_normal((400, 128)).astype(np.float32))
+        w = rng.standard_normal((1, 16)).astype(np.float32)
+        S = oracle.index_scores(q, w, k, 400, 1)[0]
+        B = oracle.score_error_bound(q, w, k, 400, 1)[0]
+        for order in orders:
+            err = np.abs(_scores_float32(q[0], w[0], k, order) - S)
+            assert np.all(err <= B), f"max err/bound {np.max(err / B):.3f}"
+
+
+def test_score_error_bound_planted_rounding_case():
+    # a planted sum whose every float32 addition rounds the same way: 2^16,
+    # then 127 products of 0.75 ulp(2^16) (q = 2^-4, k = 1.5 * 2^-4), each of
+    # which rounds up by a quarter ulp.  The bound must hold and must not be
+    # vacuous: the float32 error reaches more than a tenth of it.
+    q = np.zeros((1, 16, 128), np.uint8)
+    k = np.zeros((1, 128), np.uint8)
+    enc = lambda x: synth.encode_e4m3(np.array([x], np.float32))[0]
+    q[0, 0, 0], k[0, 0] = enc(256.0), enc(256.0)                   # 2^16
+    for d in range(1, 128):
+        q[0, 0, d], k[0, d] = enc(2.0 ** -4), enc(1.5 * 2.0 ** -4)   # 1.5 * 2^-8 = 0.75 ulp(2^16)
+    assert oracle.decode_e4m3(k[0, 1]) * oracle.decode_e4m3(q[0, 0, 1]) == 0.75 * 2.0 ** -7
+    w = np.zeros((1, 16), np.float32)
+    w[0, 0] = 1.0
+    S = oracle.index_scores(q, w, k, 1, 1)[0, 0]
+    assert S == 2.0 ** 16 + 127 * 0.75 * 2.0 ** -7
+    err = abs(_scores_float32(q[0], w[0], k, np.arange(128))[0] - S)
+    B = oracle.score_error_bound(q, w, k, 1, 1)[0, 0]
+    assert err == 127 * 0.25 * 2.0 ** -7                          # a quarter ulp up at every step
+    assert 0.1 * B < err <= B
+
+
+def test_score_error_bound_scaling_and_zero():
+    rng = np.random.default_rng(22)
+    q = synth.encode_e4m3(rng.standard_normal((2, 16, 128)).astype(np.float32))
+    k = synth.encode_e4m3(rng.standard_normal((50, 128)).astype(np.float32))
+    w = rng.standard_normal((2, 16)).astype(np.float32)
+    B = oracle.score_error_bound(q, w, k, 50, 2)
+    assert np.allclose(oracle.score_error_bound(q, -2 * w, k, 50, 2) - 1e-30, 2 * (B - 1e-30))
+    assert np.allclose(oracle.score_error_bound(q, w, k, 50, 2, rel=4e-5) - 1e-30, 2 * (B - 1e-30))
+    z = oracle.score_error_bound(np.zeros_like(q), w, k, 50, 2)
+    assert np.all(z == 1e-30)
+
+
 def test_generator_is_deterministic():
     a = synth.index_inputs(300, 2, seed=77, plant_frac=0.05)
     b = synth.index_inputs(300, 2, seed=77, plant_frac=0.05)
