@@ -34,9 +34,10 @@
  *   group of 8 fp8 products after aligning them to the group's largest
  *   exponent, keeping at least 13 fraction bits below it).
  * - Ownership: the caller owns every buffer.  The library never allocates or
- *   frees memory on a call path and keeps no global mutable state.  Scratch
- *   space is the caller's workspace `ws` of at least dsa_workspace_bytes()
- *   bytes (see the workspace contract below).
+ *   frees memory on a call path.  Scratch space is the caller's workspace `ws`
+ *   of at least dsa_workspace_bytes() bytes (see the workspace contract
+ *   below); the one exception, dsa_decode_step_noalloc, uses a static device
+ *   array per GPU instead, the library's only global mutable state.
  * - Layouts are dense, row-major, C order, with the shapes given per call.
  *   fp8 values are OCP E4M3FN bytes; bf16 values are raw 16-bit patterns.
  * - Alignment: every pointer must be 16-byte aligned (torch gives 256 B).
@@ -94,7 +95,8 @@ typedef enum dsa_status {
   DSA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement   */
   DSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
   DSA_ERR_WORKSPACE = 5,   /* ws is NULL or smaller than dsa_workspace_bytes  */
-  DSA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+  DSA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch     */
+  DSA_ERR_SCRATCH = 7      /* the request needs more than the static scratch  */
 } dsa_status;
 
 typedef enum dsa_op {
@@ -222,6 +224,31 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
                            uint16_t* out, float* lse, int32_t* idx_out,
                            float* scores_out, int64_t ld_scores,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode_step_noalloc -- dsa_decode_step without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and bits are those of dsa_decode_step.
+ *
+ * Scratch: a static device array of DSA_STATIC_SCRATCH_BYTES (64 MiB) per GPU,
+ * held from the library's first use on that GPU until the process ends; its
+ * address is looked up at the first call on each device, with that device
+ * current.  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents: a call clears on `stream` what it needs zeroed (the
+ * counter region, on the histogram path taken for T > 4), so calls in
+ * sequence are independent, but calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.  A request
+ * whose workspace (dsa_workspace_bytes(DSA_OP_DECODE_STEP, Lk, T, k, 0))
+ * exceeds the array returns DSA_ERR_SCRATCH before anything is enqueued
+ * (about 15 M keys for T = 1, 1.2 M keys for T = 8).
+ */
+#define DSA_STATIC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_decode_step_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                                   const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                   int64_t Lk, int32_t T, int32_t k, const float* sink, float sm_scale,
+                                   uint16_t* out, float* lse, int32_t* idx_out,
+                                   float* scores_out, int64_t ld_scores, void* stream);
 
 /*
  * dsa_decode_batch -- dsa_decode_step for B sequences of different lengths

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DSA_OK = 0
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
-          4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
+          4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP", 7: "DSA_ERR_SCRATCH"}
+STATIC_SCRATCH_BYTES = 64 << 20      # DSA_STATIC_SCRATCH_BYTES
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFILL_TOPK, OP_DECODE_BATCH, \
     OP_INDEX_RECALL = range(8)
 
@@ -44,6 +45,8 @@ _SIGS = {
     "swa_attn": ([_P, _P, _P, _I64, _P, _P, _I32, _I32, _P, _F, _P, _P, _P, _SZ, _P], _I32),
     "dsa_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _P, _F, _P, _P, _P, _P, _I64,
                          _P, _SZ, _P], _I32),
+    "dsa_decode_step_noalloc": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _P, _F, _P, _P, _P, _P, _I64, _P],
+                                _I32),
     "dsa_cache_append": ([_P, _P, _P, _P, _F, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
                           _P, _P, _P, _P, _P, _P], _I32),
     "dsa_prefill_topk": ([_P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
@@ -227,6 +230,19 @@ def dsa_decode_step(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: in
                                   _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
                                   _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld,
                                   ws.ptr, ws.nbytes, _stream()), "dsa_decode_step")
+    return out
+
+
+def dsa_decode_step_noalloc(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: int, sink,
+                            sm_scale: float, out, lse=None, idx_out=None, scores_out=None):
+    """dsa_decode_step on the library's static per-GPU scratch: no workspace,
+    and the C call allocates nothing (the caller passes every output)."""
+    ld = scores_out.shape[-1] if scores_out is not None else 0
+    _check(load().dsa_decode_step_noalloc(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
+                                          _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk, T, k,
+                                          _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
+                                          _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld, _stream()),
+           "dsa_decode_step_noalloc")
     return out
 
 

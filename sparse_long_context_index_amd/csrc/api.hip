@@ -2,7 +2,7 @@
 // workspace carving and launch sequencing.  Every check happens before the
 // first launch, so a rejected call enqueues nothing and touches no output.
 #include <cmath>
-#include <vector>
+#include <mutex>
 
 #include "dsa_common.hpp"
 #include "kernels.hpp"
@@ -174,6 +174,34 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+
+// ---- static scratch of the no-allocation decode step
+// Each GPU that runs the library holds one copy of this array until the
+// process ends.  Host code never passes the name itself to a kernel: on the
+// host it is only a stand-in for the symbol; the device address of each GPU's
+// copy comes from hipGetSymbolAddress at set-up.
+static __device__ __align__(256) uint8_t scratch[DSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`: its address is looked up once per
+// device, with that device current, and kept.  Returns null on a HIP error.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  g_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+
+}  // namespace
+
 }  // namespace dsa
 
 using namespace dsa;
@@ -189,6 +217,7 @@ const char* dsa_status_string(dsa_status s) {
     case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
     case DSA_ERR_HIP: return "DSA_ERR_HIP: the HIP runtime reported an error";
+    case DSA_ERR_SCRATCH: return "DSA_ERR_SCRATCH: the request needs more than the static scratch holds";
   }
   return "unknown dsa_status";
 }
@@ -345,6 +374,31 @@ dsa_status dsa_decode_step(const uint8_t* q_idx, const float* w, const uint8_t* 
   a.idx = idx; a.k_len = k; a.T = T;
   a.sink = sink; a.sm_scale = sm_scale; a.out = out; a.lse = lse;
   return hip_status(launch_sparse_attn(a, base + L.attn, st));
+}
+
+dsa_status dsa_decode_step_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache, int64_t Lk, int32_t T, int32_t k,
+                                   const float* sink, float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
+                                   float* scores_out, int64_t ld_scores, void* stream) {
+  // the same checks as dsa_decode_step, then the size limit, before any set-up
+  dsa_status s = check_index_args(q_idx, w, k_idx, Lk, T);
+  if (s != DSA_OK) return s;
+  s = check_attn_args(q, k_cache, v_cache, out, sink, lse, sm_scale);
+  if (s != DSA_OK) return s;
+  if (T > DSA_DECODE_T_MAX || k < 1 || k > DSA_TOPK_MAX) return DSA_ERR_SHAPE;
+  if ((idx_out && !aligned16(idx_out)) || (scores_out && !aligned16(scores_out))) return DSA_ERR_ALIGN;
+  if (scores_out && ld_scores < Lk) return DSA_ERR_SHAPE;
+  const size_t need = dsa_workspace_bytes(DSA_OP_DECODE_STEP, Lk, T, k, 0);
+  if (need == 0 || need > (size_t)DSA_STATIC_SCRATCH_BYTES) return DSA_ERR_SCRATCH;
+  void* ws = static_scratch();
+  if (!ws) return DSA_ERR_HIP;
+  // the scratch keeps whatever the last call left: the histogram path needs
+  // its counter region cleared first (a fill kernel, so the call can be
+  // captured); the list path reads nothing it did not write
+  if (!use_list_path(Lk, T, k) && launch_zero(ws, kCounterRegionBytes, as_stream(stream)) != hipSuccess)
+    return DSA_ERR_HIP;
+  return dsa_decode_step(q_idx, w, k_idx, q, k_cache, v_cache, Lk, T, k, sink, sm_scale, out, lse, idx_out,
+                         scores_out, ld_scores, ws, need, stream);
 }
 
 dsa_status dsa_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, const float* ln_gamma,
