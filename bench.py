@@ -10,9 +10,13 @@ instances of every input rotate so the 256 MB Infinity Cache cannot serve the
 
 Printed (one JSON line):
   value     whole-step HBM throughput = algorithmic bytes / step time (GB/s)
-  roofline  the dominant kernel (the index scan) timed with HIP events on its
-            launch stream: algorithmic bytes per launch / mean launch time,
-            against the 8 TB/s HBM peak
+  roofline  the step's dominant kernel, its index scan (idx_scan_kernel<1,
+            true>, which also leaves each workgroup's top-32 list): the scan
+            kernel nodes are taken out of a captured step and replayed alone,
+            timed with HIP events on their launch stream; algorithmic bytes
+            per launch (keys, index query, weights) / mean launch time,
+            against the 8 TB/s HBM peak and against a streaming-read ceiling
+            measured in the same run
   prefill_indexer  the fp8 MFMA contraction of an 8,192-token prefill chunk
             against 1,056,768 keys (causal): achieved TFLOP/s and % of the
             5.0 PFLOP/s dense fp8 peak
@@ -30,6 +34,11 @@ import os
 import sys
 import time
 
+# the CPU baseline's BLAS / OpenMP threads: every core this process may run on,
+# fixed before numpy is first imported (an existing setting is kept)
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(len(os.sched_getaffinity(0))))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -45,7 +54,8 @@ BYTES_KEYS = LK * 128
 BYTES_GATHER = K * 4 * (192 + 128) * 2
 BYTES_SMALL = T * 64 * 192 * 2 + T * 64 * 128 * 2 + T * 16 * 128 + T * 16 * 4 + 64 * 4
 STEP_BYTES = BYTES_KEYS + BYTES_GATHER + BYTES_SMALL            # 139,504,064
-SCAN_BYTES = BYTES_KEYS + T * 16 * 128 + T * 16 * 4 + T * LK * 4  # keys + q + w + scores out
+SCAN_BYTES = BYTES_KEYS + T * 16 * 128 + T * 16 * 4 + T * LK * 4  # standalone scan: keys + q + w + scores out
+LIST_SCAN_BYTES = BYTES_KEYS + T * 16 * 128 + T * 16 * 4         # the step's scan: keys + q + w (134,219,968)
 
 PREFILL_T, PREFILL_L = 8192, 1048576
 PREFILL_LK = PREFILL_L + PREFILL_T
@@ -130,7 +140,15 @@ def main():
     ms_replay, wall_ms = replay_ms(torch, g_step, reps)
     ms_step = ms_replay / ROTATE
 
-    # dominant kernel: the index scan, launched alone on the same stream
+    # the step's dominant kernel: its index scan, replayed alone (kernel nodes
+    # taken from a captured step)
+    try:
+        ms_list_scan = time_step_scan(torch, step, reps)
+        scan_err = None
+    except (RuntimeError, OSError) as e:              # reported, and the standalone scan stands in
+        ms_list_scan, scan_err = None, str(e)
+
+    # the standalone scan (dsa_index_scores, which also stores the scores)
     scores = [torch.empty((T, LK), dtype=torch.float32, device=dev) for _ in range(ROTATE)]
 
     def scan(i):
@@ -145,6 +163,18 @@ def main():
     g_scan = capture(torch, lambda: [scan(i) for i in range(4 * ROTATE)])
     ms_scan = replay_ms(torch, g_scan, reps)[0] / (4 * ROTATE)
     scan_gbs = SCAN_BYTES / (ms_scan * 1e-3) / 1e9
+    # the best streaming rate seen in this run: torch's own sum and copy over
+    # 1 GiB, and this library's standalone scan (a read stream of the keys)
+    ceiling = read_ceiling(torch, dev)
+    ceiling["all"]["standalone scan"] = round(scan_gbs, 1)
+    if scan_gbs > ceiling["GB/s"]:
+        ceiling["GB/s"], ceiling["kernel"] = round(scan_gbs, 1), "idx_scan_kernel<1, false> (standalone scan)"
+    if ms_list_scan is not None:
+        rl_kernel, rl_bytes, rl_ms = "idx_scan_kernel<1, true> (the decode step's index scan)", LIST_SCAN_BYTES, ms_list_scan
+    else:
+        rl_kernel, rl_bytes, rl_ms = "idx_scan_kernel<1, false> (dsa_index_scores; step scan untimed: " + scan_err + ")", \
+            SCAN_BYTES, ms_scan
+    rl_gbs = rl_bytes / (rl_ms * 1e-3) / 1e9
 
     result = {
         "metric": "DSA decode-step µs & HBM GB/s (% peak) at 1M ctx; prefill indexer fp8 MFMA %",
@@ -164,10 +194,17 @@ def main():
         "config": {"workload": "dsa_decode_1m", "history": L, "query_tokens": T, "topk": K,
                    "idx_heads": 16, "q_heads": 64, "kv_heads": 4, "qk_dim": 192, "v_dim": 128,
                    "algorithmic_bytes_per_step": STEP_BYTES, "rotation_instances": ROTATE},
-        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel<1, false> (dsa_index_scores, T=1)",
-                     "achieved": round(scan_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": SCAN_BYTES, "us_per_launch": round(ms_scan * 1e3, 3)},
+        "roofline": {"bound": "hbm", "kernel": rl_kernel,
+                     "achieved": round(rl_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rl_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if ms_list_scan is not None else None,
+                     "bytes_per_launch": rl_bytes, "us_per_launch": round(rl_ms * 1e3, 3),
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": round(rl_gbs / ceiling["GB/s"], 4),
+                     "standalone_scan": {"kernel": "idx_scan_kernel<1, false> (dsa_index_scores, scores stored)",
+                                         "bytes_per_launch": SCAN_BYTES, "us_per_launch": round(ms_scan * 1e3, 3),
+                                         "achieved": round(scan_gbs, 2),
+                                         "frac": round(scan_gbs / HBM_PEAK_GBS, 4)}},
         "host_wall_ms_per_step": round(wall_ms / n_steps, 6),
         "launch": "hip graph of one step per rotation instance, replayed",
         "input_gen_s": round(gen_s, 2),
@@ -196,9 +233,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "idx_scan_dsa_decode_1m_traffic.js
 
 
 def measured_traffic():
-    """HBM bytes per scan launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (copy-calibrated), or None when the scan's sources have
-    changed since those counters were taken."""
+    """HBM bytes per launch of the step's scan from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (copy-calibrated), or None when the scan's
+    sources have changed since those counters were taken."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -207,9 +244,113 @@ def measured_traffic():
             h.update(open(os.path.join(ROOT, p), "rb").read())
         if h.hexdigest() != rec["source_sha256"]:
             return None
-        return int(rec["traffic_bytes_per_launch"])
+        return int(rec["in_step_list_scan"]["traffic_bytes"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def time_step_scan(torch, step, reps):
+    """Mean launch time (ms) of the decode step's scan kernel alone.  One step
+    per rotation instance is captured on a side stream (HIP stream capture
+    through the runtime torch already loaded); the scan kernel nodes -- the
+    grid of 512 x 256-thread workgroups -- are copied, with their captured
+    arguments, into a graph that chains them 4 times over, and that graph is
+    replayed between HIP events on the same stream."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")          # the runtime torch loaded
+
+    class Dim3(ctypes.Structure):
+        _fields_ = [("x", ctypes.c_uint), ("y", ctypes.c_uint), ("z", ctypes.c_uint)]
+
+    class KernelNodeParams(ctypes.Structure):      # hipKernelNodeParams
+        _fields_ = [("blockDim", Dim3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                    ("gridDim", Dim3), ("kernelParams", ctypes.c_void_p), ("sharedMemBytes", ctypes.c_uint)]
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = ctypes.c_void_p()
+    with torch.cuda.stream(side):
+        ok(hip.hipStreamBeginCapture(ctypes.c_void_p(side.cuda_stream), 0), "hipStreamBeginCapture")
+        for i in range(ROTATE):
+            step(i)
+        ok(hip.hipStreamEndCapture(ctypes.c_void_p(side.cuda_stream), ctypes.byref(graph)), "hipStreamEndCapture")
+    n = ctypes.c_size_t(0)
+    ok(hip.hipGraphGetNodes(graph, None, ctypes.byref(n)), "hipGraphGetNodes")
+    nodes = (ctypes.c_void_p * n.value)()
+    ok(hip.hipGraphGetNodes(graph, nodes, ctypes.byref(n)), "hipGraphGetNodes")
+    scans = []
+    for node in nodes:
+        ty = ctypes.c_int(-1)
+        ok(hip.hipGraphNodeGetType(ctypes.c_void_p(node), ctypes.byref(ty)), "hipGraphNodeGetType")
+        if ty.value != 0:                          # hipGraphNodeTypeKernel
+            continue
+        p = KernelNodeParams()
+        ok(hip.hipGraphKernelNodeGetParams(ctypes.c_void_p(node), ctypes.byref(p)), "hipGraphKernelNodeGetParams")
+        # the grid may be recorded in workgroups or in threads
+        if (p.gridDim.x in (512, 512 * 256) and (p.gridDim.y, p.gridDim.z) == (1, 1)
+                and (p.blockDim.x, p.blockDim.y, p.blockDim.z) == (256, 1, 1)):
+            scans.append(p)
+    if len(scans) != ROTATE:
+        raise RuntimeError(f"expected {ROTATE} scan kernel nodes, found {len(scans)}")
+    g2 = ctypes.c_void_p()
+    ok(hip.hipGraphCreate(ctypes.byref(g2), 0), "hipGraphCreate")
+    prev = None
+    for _ in range(4):
+        for p in scans:
+            node = ctypes.c_void_p()
+            deps = (ctypes.c_void_p * 1)(prev) if prev is not None else None
+            ok(hip.hipGraphAddKernelNode(ctypes.byref(node), g2, deps, 1 if prev is not None else 0, ctypes.byref(p)),
+               "hipGraphAddKernelNode")
+            prev = node.value
+    exe = ctypes.c_void_p()
+    ok(hip.hipGraphInstantiate(ctypes.byref(exe), g2, None, None, 0), "hipGraphInstantiate")
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    for _ in range(3):
+        ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * 4 * ROTATE)
+    hip.hipGraphExecDestroy(exe)
+    hip.hipGraphDestroy(g2)
+    hip.hipGraphDestroy(graph)
+    return ms
+
+
+def read_ceiling(torch, dev, nbytes=1 << 30):
+    """The streaming rates torch's own kernels reach over 1 GiB in this run:
+    a float32 sum (reads N bytes) and a device copy (reads and writes N,
+    counted as 2 N), each the best of 5 timed runs.  A reference point for
+    what a plain stream achieves on this machine, not a bound of the kernels."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, moved in (("sum", lambda: x.sum(), nbytes), ("copy", lambda: y.copy_(x), 2 * nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None or ms < best else best
+        out[name] = round(moved / (best * 1e-3) / 1e9, 1)
+    del x, y
+    k = max(out, key=out.get)
+    return {"GB/s": out[k], "kernel": f"torch {k} over 1 GiB", "all": out}
 
 
 def capture(torch, fn):
@@ -274,17 +415,18 @@ def bench_prefill(torch, np, binding, synth, dev, chunk=1024, reps=2):
            "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "bound": "mfma",
            "score_bytes_written": PREFILL_T * PREFILL_LK * 4}
     del scores
-    # the fused index scores + top-2,048 of every row (no score matrix); the
-    # call reads one word back, so it is timed on the host around a sync
+    # the fused index scores + top-2,048 of every row (no score matrix; the
+    # selection on exact scores), timed with HIP events
     ws = binding.Workspace(binding.workspace_bytes(binding.OP_PREFILL_TOPK, PREFILL_LK, PREFILL_T, 2048))
     idx = torch.empty((PREFILL_T, 2048), dtype=torch.int32, device=dev)
     binding.dsa_prefill_topk(qd, wd, kd, PREFILL_LK, PREFILL_T, 2048, idx=idx, ws=ws)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0.record(st)
     for _ in range(reps):
         binding.dsa_prefill_topk(qd, wd, kd, PREFILL_LK, PREFILL_T, 2048, idx=idx, ws=ws)
+    e1.record(st)
     torch.cuda.synchronize()
-    ms_f = (time.perf_counter() - t0) * 1e3 / reps
+    ms_f = e0.elapsed_time(e1) / reps
     tf_f = prefill_flops() / (ms_f * 1e-3) / 1e12
     res["fused_topk"] = {"workload": "dsa_prefill_1m_t8k index scores + top-2048 per row (fused)",
                          "ms": round(ms_f, 3), "achieved": round(tf_f, 1), "unit": "TFLOP/s",
@@ -477,20 +619,33 @@ def bench_swa(torch, np, binding, synth, dev, reps):
             "bound": "hbm (latency at this size)"}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(d, n_steps):
-    """The fp64 oracle's full decode step on a bounded sample of steps."""
+    """The fp64 oracle's full decode step on a bounded sample of steps.  Its
+    BLAS threads were fixed before numpy's import (module top); `cores` is
+    the thread count the BLAS reports using."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     import oracle
     t0 = time.perf_counter()
     for _ in range(n_steps):
         oracle.dsa_decode_step(d, K)
     per = (time.perf_counter() - t0) / n_steps
     return {"value": round(STEP_BYTES / per / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "s_per_step": round(per, 3),
+            "kind": "oracle", "s_per_step": round(per, 3), "cpu_model": cpu_model(),
+            "cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n_steps} full dsa_decode_1m steps (fp64 numpy oracle, same inputs)"}
 
 

@@ -87,7 +87,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
     const int tile = rd * NW + wave;
     const bool active = wave_on && tile < ntiles;   // wave-uniform
     const int tb = p0 + tile * kTileKeys;
-    bf16x8 pf;
+    bf16x8 pf, pl;           // P as bf16 high and low parts: pf + pl carries ~16 bits of each probability
     if (active) {
       // ---- all index and row loads first: one dependent round trip per tile.
       // Every load instruction reads whole runs of a few rows: K, 64 bytes of
@@ -159,7 +159,9 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
         for (int i = 0; i < 4; ++i) {
           const float pv = dead ? 0.0f : exp2f(z[b][i] - mn);
           ps += pv;
-          pf[b * 4 + i] = (__bf16)pv;
+          const __bf16 hi = (__bf16)pv;
+          pf[b * 4 + i] = hi;
+          pl[b * 4 + i] = (__bf16)(pv - (float)hi);
         }
       lsum = lsum * alpha + ps;
       m = mn;
@@ -183,6 +185,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
           vb[e] = vs[kk * kVStride + blk * 16 + col];
         }
         o[blk] = mfma_bf16_16x16x32(pf, __builtin_bit_cast(bf16x8, vb), o[blk]);
+        o[blk] = mfma_bf16_16x16x32(pl, __builtin_bit_cast(bf16x8, vb), o[blk]);
       }
     }
     __syncthreads();
