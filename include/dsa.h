@@ -316,14 +316,14 @@ dsa_status dsa_index_recall(const uint16_t* q, const uint16_t* k_cache, const ui
  * Internally the fp8 MFMA contraction only locates candidates: scores of
  * every 64th key give each row a threshold theta; one pass over all keys
  * keeps the keys whose fp8 score reaches theta minus the largest error that
- * score can have (bounded per 2048-key tile from the row's query norms and
- * the tile's largest key norm), up to 8192 per row; the candidates are
+ * score can have (bounded per key from the row's query and weights and the
+ * key's norm), up to 12,288 per row; the candidates are
  * re-scored exactly and the top-k selected from them once at least min(k,
  * p_t+1) of them reach theta (then no key left out can belong).  A row that
  * fails this is recomputed exactly on the device, so the result never
  * depends on the threshold.  Nothing is read back to the host.
  * Limits: 1 <= T <= Lk < 2^31, 1 <= k <= 2048.  Needs ws (DSA_OP_PREFILL_TOPK,
- * about T * (Lk / 16 + 64 KiB) + min(T, 64) * Lk * 4 bytes).
+ * about T * (Lk / 16 + 96 KiB) + (min(T, 64) + 1) * Lk * 4 bytes).
  */
 dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int32_t T,
                             int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);

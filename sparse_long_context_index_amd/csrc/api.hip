@@ -87,7 +87,7 @@ DecodeLayout decode_layout(int64_t Lk, int T, int k) {
 
 // workspace of the fused prefill top-k
 struct PrefillLayout {
-  size_t sample, theta, cw, tnorm, count, failed, cand, fb, total;
+  size_t sample, theta, cw, knorm, count, failed, cand, fb, total;
   int64_t ld_sample, ld_fb;
   int fb_blocks;
 };
@@ -104,8 +104,8 @@ PrefillLayout prefill_layout(int64_t Lk, int T) {
   off += align_up((size_t)T * sizeof(uint32_t));
   d.cw = off;
   off += align_up((size_t)T * sizeof(float));
-  d.tnorm = off;
-  off += align_up((size_t)cdiv(Lk, kPrefillTileKeys) * sizeof(float));
+  d.knorm = off;
+  off += align_up((size_t)Lk * sizeof(float));
   d.count = off;                               // T row counters, then the failure count
   off += align_up(((size_t)T + 4) * sizeof(uint32_t));
   d.failed = off;
@@ -523,9 +523,9 @@ dsa_status dsa_prefill_topk(const uint8_t* q_idx, const float* w, const uint8_t*
   uint32_t* failed = reinterpret_cast<uint32_t*>(base + d.failed);
   PrefillCand pc{theta, count, reinterpret_cast<uint2*>(base + d.cand), kPrefillCap};
   pc.cw = reinterpret_cast<float*>(base + d.cw);
-  pc.tnorm = reinterpret_cast<float*>(base + d.tnorm);
+  pc.knorm = reinterpret_cast<float*>(base + d.knorm);
   hipError_t e = launch_zero(count, align_up(((size_t)T + 4) * sizeof(uint32_t)), st);
-  if (e == hipSuccess) e = launch_key_tile_norms(k_idx, Lk, const_cast<float*>(pc.tnorm), st);
+  if (e == hipSuccess) e = launch_key_norms(k_idx, Lk, const_cast<float*>(pc.knorm), st);
   if (e == hipSuccess) e = launch_idx_gemm_sample(q_idx, w, k_idx, Lk, T, kPrefillStep, sample, d.ld_sample, st);
   if (e == hipSuccess)
     e = launch_prefill_theta(sample, d.ld_sample, q_idx, w, Lk, T, kPrefillStep, k, kPrefillCap, theta,

@@ -136,11 +136,10 @@ hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const ui
 // candidate emission: every visible key whose order key reaches theta[t] is
 // appended to row t's slots as (order key, index); count[t] counts them all
 // (slots past cap are not written)
-// A key is a candidate of row t when the contraction's score reaches theta[t]
-// lowered by cw[t] * tnorm[tile]: cw[t] bounds, per unit of key norm, how far
-// the contraction's score of row t can lie from the exact one (see the fused
-// prefill top-k), tnorm[tile] is the largest key norm of the key's
-// kPrefillTileKeys-key tile.
+// A key s is a candidate of row t when the contraction's score plus
+// cw[t] * knorm[s] reaches theta[t]: cw[t] bounds, per unit of key norm, how
+// far the contraction's score of row t can lie from the exact one (see the
+// fused prefill top-k), knorm[s] bounds the key's norm.
 constexpr int kPrefillTileKeys = 2048;
 struct PrefillCand {
   const uint32_t* theta;   // [T]
@@ -148,22 +147,21 @@ struct PrefillCand {
   uint2* cand;             // [T][cap]
   int cap;
   const float* cw = nullptr;     // [T]
-  const float* tnorm = nullptr;  // [ceil(Lk / kPrefillTileKeys)]
+  const float* knorm = nullptr;  // [Lk]
 };
 hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                                 const PrefillCand& pc, hipStream_t st);
 
 // ---- fused prefill top-k (prefill_topk.hip)
 constexpr int kPrefillStep = 64;           // key sample stride of the threshold estimate
-constexpr int kPrefillCap = 8192;          // candidate slots per row
+constexpr int kPrefillCap = 12288;         // candidate slots per row
 constexpr int kPrefillFallbackBlocks = 64; // workgroups (and score rows of workspace) of the exact fallback
 size_t prefill_refine_lds(int cap);
-// tnorm[j]: an upper bound of the largest Euclidean norm of keys
-// j * kPrefillTileKeys .. (j + 1) * kPrefillTileKeys - 1 (below Lk)
-hipError_t launch_key_tile_norms(const uint8_t* k_idx, int64_t Lk, float* tnorm, hipStream_t st);
+// knorm[s]: an upper bound of the Euclidean norm of key s
+hipError_t launch_key_norms(const uint8_t* k_idx, int64_t Lk, float* knorm, hipStream_t st);
 // theta[t]: order key of the row's threshold (0: every visible key); cw[t]:
-// the row's error factor (sum_h |w[t,h]| |q_idx[t,h]| times the relative
-// error bound of the contraction, rounded up)
+// the row's error factor (|u| with u_d = sum_h |w[t,h]| |q_idx[t,h,d]|, times
+// the relative error bound of the contraction, rounded up)
 hipError_t launch_prefill_theta(const float* sample, int64_t ld, const uint8_t* q_idx, const float* w, int64_t Lk,
                                 int T, int step, int k, int cap, uint32_t* theta, float* cw, hipStream_t st);
 // the candidates' order keys recomputed with the exact index arithmetic (in place)

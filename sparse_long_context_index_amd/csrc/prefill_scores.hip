@@ -147,23 +147,23 @@ __device__ __forceinline__ float order_key_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// The candidate test of a row against a key tile: the row's threshold lowered
-// by the largest difference between this contraction's score and the exact
-// one that any key of the tile can show (cw = the row's error factor, tn = the
-// tile's largest key norm), formed in double and rounded down, never below
-// the lowest finite float (so a masked key, scored -inf, never passes).
-__device__ __forceinline__ float lowered_threshold(uint32_t theta, float cw, float tn) {
-  constexpr float kLowest = -3.402823466e38f;
-  if (theta == 0u) return kLowest;
-  const float f = __double2float_rd((double)order_key_to_float(theta) - (double)cw * (double)tn);
-  return f > kLowest ? f : kLowest;
+// The candidate test of a row: score + cw * n_s >= the returned value, where
+// cw * n_s bounds how far this contraction's score of key s can lie from the
+// exact one.  The row's threshold is lowered by 2^-20 of its magnitude, which
+// covers the float rounding of the test's product and sum.  No threshold
+// (order key 0) gives the lowest finite float, which every finite score
+// passes and a masked key (-inf) does not.
+__device__ __forceinline__ float cand_threshold(uint32_t theta) {
+  if (theta == 0u) return -3.402823466e38f;
+  const float f = order_key_to_float(theta);
+  return f - fabsf(f) * (1.0f / 1048576.0f);
 }
 
 enum GemmMode { kGemmScores = 0, kGemmSample = 1, kGemmCand = 2 };
 
 struct GemmArgs {
   const float* cw;     // candidate mode: [T] per-row error factor (see PrefillCand)
-  const float* tnorm;  // candidate mode: [key tiles] largest key norm of each 2048-key tile
+  const float* knorm;  // candidate mode: [Lk] key norm bounds
   const uint8_t* q_idx;
   const float* w;
   const uint8_t* k_idx;
@@ -178,8 +178,17 @@ struct GemmArgs {
   int64_t n_ttiles, n_ktiles, per_xcd;
 };
 
+// Waves per SIMD the launch bounds ask for, and key blocks in flight per wave.
+// The candidate mode keeps more state per lane: with 4 blocks in flight it
+// spills at 3 waves per SIMD (46.8 ms for the 8,192-token chunk's fused
+// top-k), at 2 waves it takes 26.4 ms, with 2 blocks in flight at 3 waves
+// 23.3 ms.
+template <int kMode> struct GemmShape { static constexpr int waves = 3, pf = kGemmPF; };
+template <> struct GemmShape<2> { static constexpr int waves = 3, pf = 2; };
+
 template <int kMode>
-__global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
+__global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(GemmArgs ga) {
+  constexpr int PF = GemmShape<kMode>::pf;
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
   // range of logical tiles, ordered so consecutive tiles share a key tile
   // and a group of token tiles stays resident in that XCD's L2.
@@ -214,6 +223,15 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
   const int grp = lane >> 4;
   const int t0 = (int)(ttile * kGemmTok) + wave * 8;
   const int64_t s0 = ktile * kGemmKeys;                // first key of the tile, in key-space units
+  // candidate mode: the norm bounds of the tile's keys, staged in LDS once
+  __shared__ float nsm[kMode == kGemmCand ? kGemmKeys : 1];
+  if (kMode == kGemmCand) {
+    for (int i = threadIdx.x; i < kGemmKeys; i += 256) {
+      const int64_t key = s0 + i;
+      nsm[i] = ga.knorm[key < Lk ? key : Lk - 1];
+    }
+    __syncthreads();
+  }
   if (t0 >= T) return;                                 // wave-uniform
 
   // the wave's 8 x 16 head weights sit in LDS (registers go to the operands)
@@ -241,10 +259,10 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
     return load_frag32_cached(ga.k_idx + (key < last ? key : last) * 128 + 32 * grp);
   };
   constexpr int NB = kGemmKeys / 16;
-  static_assert(NB % kGemmPF == 0, "whole prefetch rounds");
-  i32x8 b[kGemmPF];
+  static_assert(NB % PF == 0 && PF <= kGemmPF, "whole prefetch rounds");
+  i32x8 b[PF];
 #pragma unroll
-  for (int u = 0; u < kGemmPF; ++u) b[u] = load_b(u);
+  for (int u = 0; u < PF; ++u) b[u] = load_b(u);
   const int64_t end = ga.nkeys - s0 < kGemmKeys ? ga.nkeys - s0 : kGemmKeys;   // keys of this tile
   __shared__ __attribute__((aligned(16))) float stage[kMode == kGemmCand ? 1 : 4][8 * kStageStride];
   float* st = stage[kMode == kGemmCand ? 0 : wave];
@@ -254,19 +272,27 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
   uint32_t c0 = 0, c1 = 0;
   __shared__ uint2 lcand[kMode == kGemmCand ? 4 : 1][kMode == kGemmCand ? 8 * kLocalCand : 1];
   __shared__ uint32_t lcnt[kMode == kGemmCand ? 4 : 1][8];
+  float cw0 = 0.f, cw1 = 0.f;
   if (kMode == kGemmCand) {
-    const float tn = ga.tnorm[ktile];
-    if (t0 + grp < T) th0 = lowered_threshold(ga.cand.theta[t0 + grp], ga.cw[t0 + grp], tn);
-    if (t0 + grp + 4 < T) th1 = lowered_threshold(ga.cand.theta[t0 + grp + 4], ga.cw[t0 + grp + 4], tn);
+    if (t0 + grp < T) {
+      th0 = cand_threshold(ga.cand.theta[t0 + grp]);
+      cw0 = ga.cw[t0 + grp];
+    }
+    if (t0 + grp + 4 < T) {
+      th1 = cand_threshold(ga.cand.theta[t0 + grp + 4]);
+      cw1 = ga.cw[t0 + grp + 4];
+    }
   }
+
 #pragma unroll 1
-  for (int kb = 0; kb < NB; kb += kGemmPF) {
+  for (int kb = 0; kb < NB; kb += PF) {
     if ((int64_t)kb * 16 >= end) break;                // wave-uniform
 #pragma unroll
-    for (int u = 0; u < kGemmPF; ++u) {
+    for (int u = 0; u < PF; ++u) {
       const i32x8 cur = b[u];
-      const int nb = kb + kGemmPF + u;
+      const int nb = kb + PF + u;
       b[u] = load_b(nb < NB ? nb : NB - 1);           // unconditional: no branch around the load
+
       const int64_t kk = (s0 + (kb + u) * 16) * step;
       const float2 v = gemm_block(a, wv, cur, kk, step, t0, Lk, T, col, grp);
       if (kMode == kGemmCand) {
@@ -274,7 +300,8 @@ __global__ __launch_bounds__(256, 3) void idx_gemm_kernel(GemmArgs ga) {
         // threshold: masked keys score -inf, which no threshold admits, and
         // tokens beyond T have threshold +inf
         const int64_t key = kk + col;
-        const bool ok0 = v.x >= th0, ok1 = v.y >= th1;
+        const float ncur = nsm[(kb + u) * 16 + col];
+        const bool ok0 = v.x + cw0 * ncur >= th0, ok1 = v.y + cw1 * ncur >= th1;
         const uint32_t k0 = order_key(v.x), k1 = order_key(v.y);
         const uint64_t m0 = __ballot(ok0), m1 = __ballot(ok1);
         if (m0 | m1) {                                 // wave-uniform
@@ -355,11 +382,11 @@ hipError_t launch_idx_gemm_sample(const uint8_t* q_idx, const float* w, const ui
 
 hipError_t launch_idx_gemm_cand(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t Lk, int T,
                                 const PrefillCand& pc, hipStream_t st) {
-  if (pc.cap < 1 || !pc.theta || !pc.count || !pc.cand || !pc.cw || !pc.tnorm) return hipErrorInvalidValue;
+  if (pc.cap < 1 || !pc.theta || !pc.count || !pc.cand || !pc.cw || !pc.knorm) return hipErrorInvalidValue;
   GemmArgs ga = gemm_args(q_idx, w, k_idx, Lk, T, 1);
   ga.cand = pc;
   ga.cw = pc.cw;
-  ga.tnorm = pc.tnorm;
+  ga.knorm = pc.knorm;
   return launch_gemm<kGemmCand>(ga, st);
 }
 

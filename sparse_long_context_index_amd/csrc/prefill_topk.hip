@@ -8,18 +8,17 @@
 // The fp8 MFMA contraction (prefill_scores.hip) only locates candidates; the
 // selection is made on exact scores (the decode scan's arithmetic), so the
 // result is the top-k of the exact scores, row for row:
-//  1. key_tile_norm_kernel: per 2048-key tile, an upper bound N_j of the
-//     largest key norm;
+//  1. key_norm_kernel: an upper bound n_s of every key's Euclidean norm;
 //  2. the contraction over a strided sample of the keys (every 64th) writes a
 //     small score matrix; prefill_theta_kernel takes per row the r-th largest
-//     sampled score as the row's threshold theta (about max(2.5 k, 4096) keys
-//     of the row reach it, against 8192 candidate slots; no threshold when
+//     sampled score as the row's threshold theta (about max(2 k, 4096) keys
+//     of the row reach it, against 12,288 candidate slots; no threshold when
 //     the row's visible keys fit the slots), and the row's error factor
-//     c_t = c * sum_h |w_h| |q_h| (c bounds the contraction's error relative
-//     to sum_h |w_h| sum_d |q_hd k_d|, which Cauchy-Schwarz bounds by
-//     sum_h |w_h| |q_h| |k|);
-//  3. the contraction over all keys appends every visible key whose score
-//     reaches theta - c_t N_j to the row's slots: no key whose exact score
+//     c_t = c |u| with u_d = sum_h |w_h| |q_hd| (c bounds the contraction's
+//     error relative to sum_h |w_h| sum_d |q_hd k_d| = u . |k|, which
+//     Cauchy-Schwarz bounds by |u| |k|);
+//  3. the contraction over all keys appends every visible key s whose score
+//     plus c_t n_s reaches theta to the row's slots: no key whose exact score
 //     reaches theta is missed;
 //  4. prefill_rescore_kernel recomputes the candidates' scores exactly;
 //  5. prefill_refine_kernel checks that at least min(k, visible keys)
@@ -55,32 +54,24 @@ __global__ __launch_bounds__(kPtNT) void prefill_theta_kernel(const float* __res
                                                               int rank, int cap, uint32_t* __restrict__ theta,
                                                               float* __restrict__ cw) {
   __shared__ RadixShared rs;
-  __shared__ double hsum[16];
+  __shared__ double usq[2];
   const int t = blockIdx.x;
   const int64_t p = Lk - T + t;
-  if (threadIdx.x < 16) {
-    // |q_h| of head h in double (the squares of e4m3 values and their sums are exact)
-    const uint8_t* qh = q_idx + ((size_t)t * 16 + threadIdx.x) * 128;
-    double ss = 0.0;
-    for (int d = 0; d < 128; d += 32) {
-      bf16x8 v[4];
-      widen_fp8(load_frag32_cached(qh + d), v);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double x = (double)(float)v[s4][e];
-          ss += x * x;
-        }
+  if (threadIdx.x < 128) {
+    // u_d = sum_h |w_h| |q_hd| and |u|^2 in double (thread d; two waves)
+    double u = 0.0;
+    for (int h = 0; h < 16; ++h) {
+      const uint8_t code = q_idx[((size_t)t * 16 + h) * 128 + threadIdx.x];
+      const bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)code, 1.0f, false);
+      u += fabs((double)w[(size_t)t * 16 + h]) * fabs((double)(float)v[0]);
     }
-    hsum[threadIdx.x] = fabs((double)w[(size_t)t * 16 + threadIdx.x]) * sqrt(ss);
+    double sq = u * u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+    if ((threadIdx.x & 63) == 0) usq[threadIdx.x >> 6] = sq;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double W = 0.0;
-    for (int h = 0; h < 16; ++h) W += hsum[h];
-    cw[t] = __double2float_ru(W * kCandRel * (1.0 + 1.0 / 1048576.0));
-  }
+  if (threadIdx.x == 0) cw[t] = __double2float_ru(sqrt(usq[0] + usq[1]) * kCandRel * (1.0 + 1.0 / 1048576.0));
   if (p + 1 <= cap) {                                  // every visible key fits: no threshold
     if (threadIdx.x == 0) theta[t] = 0u;
     return;
@@ -93,46 +84,27 @@ __global__ __launch_bounds__(kPtNT) void prefill_theta_kernel(const float* __res
   if (threadIdx.x == 0) theta[t] = tau;
 }
 
-// Upper bound of the largest key norm of each kPrefillTileKeys-key tile: four
-// lanes per key each widen 32 bytes and sum their squares in double (exact),
-// the key's sum of 128 squares is exact, its square root rounded up to float.
-__global__ __launch_bounds__(256) void key_tile_norm_kernel(const uint8_t* __restrict__ k_idx, int64_t Lk,
-                                                            float* __restrict__ tnorm) {
-  __shared__ float red[4];
-  const int64_t base = (int64_t)blockIdx.x * kPrefillTileKeys;
-  const int lane = threadIdx.x & 63;
-  float m = 0.f;
-  for (int j = threadIdx.x >> 2; j < kPrefillTileKeys; j += 64) {
-    const int64_t key = base + j;
-    double ss = 0.0;
-    if (key < Lk) {
-      bf16x8 v[4];
-      widen_fp8(load_frag32_cached(k_idx + key * 128 + 32 * (threadIdx.x & 3)), v);
+// Upper bound of every key's Euclidean norm: four lanes per key each widen 32
+// bytes and sum their squares in double (exact), the key's sum of 128
+// squares is exact, its square root rounded up to float.
+__global__ __launch_bounds__(256) void key_norm_kernel(const uint8_t* __restrict__ k_idx, int64_t Lk,
+                                                       float* __restrict__ knorm) {
+  const int64_t key = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  double ss = 0.0;
+  if (key < Lk) {
+    bf16x8 v[4];
+    widen_fp8(load_frag32_cached(k_idx + key * 128 + 32 * (threadIdx.x & 3)), v);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double x = (double)(float)v[s4][e];
-          ss += x * x;
-        }
-    }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    const float nrm = __double2float_ru(sqrt(ss) * (1.0 + 1.0 / 1048576.0));
-    m = m > nrm ? m : nrm;
+      for (int e = 0; e < 8; ++e) {
+        const double x = (double)(float)v[s4][e];
+        ss += x * x;
+      }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float y = __shfl_xor(m, o, 64);
-    m = m > y ? m : y;
-  }
-  if (lane == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int i = 1; i < 4; ++i) r = r > red[i] ? r : red[i];
-    tnorm[blockIdx.x] = r;
-  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  if (key < Lk && (threadIdx.x & 3) == 0) knorm[key] = __double2float_ru(sqrt(ss) * (1.0 + 1.0 / 1048576.0));
 }
 
 // Exact scores of the candidates: block (t, y) takes candidates 256 y ..
@@ -216,18 +188,18 @@ __global__ __launch_bounds__(kPtNT) void prefill_refine_kernel(PrefillCand pc, i
 
 size_t prefill_refine_lds(int cap) { return sizeof(RefineShared) + (size_t)cap * 8; }
 
-hipError_t launch_key_tile_norms(const uint8_t* k_idx, int64_t Lk, float* tnorm, hipStream_t st) {
-  const int64_t tiles = cdiv(Lk, kPrefillTileKeys);
-  if (tiles < 1 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(key_tile_norm_kernel, dim3((unsigned)tiles), dim3(256), 0, st, k_idx, Lk, tnorm);
+hipError_t launch_key_norms(const uint8_t* k_idx, int64_t Lk, float* knorm, hipStream_t st) {
+  const int64_t blocks = cdiv(Lk, 64);
+  if (blocks < 1 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)blocks), dim3(256), 0, st, k_idx, Lk, knorm);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_theta(const float* sample, int64_t ld, const uint8_t* q_idx, const float* w, int64_t Lk,
                                 int T, int step, int k, int cap, uint32_t* theta, float* cw, hipStream_t st) {
-  // about 2.5 k (at least 64 step) keys of the whole row reach the rank-th
+  // about 2 k (at least 64 step) keys of the whole row reach the rank-th
   // largest sampled score; a rank of 64 or more keeps the estimate steady
-  int rank = (int)cdiv((int64_t)5 * k, 2 * (int64_t)step);
+  int rank = (int)cdiv((int64_t)2 * k, (int64_t)step);
   if (rank < 64) rank = 64;
   if ((int64_t)rank * step * 3 / 2 > cap) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prefill_theta_kernel, dim3(T), dim3(kPtNT), 0, st, sample, ld, q_idx, w, Lk, T, step, rank, cap,
