@@ -112,14 +112,13 @@ __device__ __forceinline__ float exact_score(const ExactQuery& eq, const i32x8& 
 // Exact scores of query token q_t / w_t against keys 0 .. n - 1 into row,
 // by the NT threads of a workgroup (each wave takes 16-key tiles, U tiles'
 // loads in flight).  Plain stores: the caller synchronises before reading.
-template <int NT>
+template <int NT, int U>
 __device__ __forceinline__ void exact_scores_block(const uint8_t* q_t, const float* w_t, const uint8_t* k_idx,
                                                    int64_t n, float* row) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   ExactQuery eq;
   load_exact_query(q_t, w_t, eq);
-  constexpr int U = 8;
   const int64_t ntiles = cdiv(n, 16);
   for (int64_t t0 = (int64_t)wave * U; t0 < ntiles; t0 += (int64_t)(NT / 64) * U) {
     i32x8 kr[U];

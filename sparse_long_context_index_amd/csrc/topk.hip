@@ -488,7 +488,7 @@ struct RowSel {
 
 // The top-k of one scores row of n visible keys into out_row[0 .. k), by the
 // kRowThreads threads of a workgroup (the shared structures are the caller's).
-__device__ void row_topk(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out_row,
+__device__ __forceinline__ void row_topk(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out_row,
                          RowShared& rsh, RowSel& sh, FinalShared& fs) {
   const int lane = threadIdx.x & 63;
 
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_fallback_kernel(
     const uint32_t t = failed[i];
     if (t >= (uint32_t)T) continue;                    // block-uniform; never written so by the refine kernel
     const int64_t n = Lk - T + (int64_t)t + 1;
-    exact_scores_block<kRowThreads>(q_idx + (size_t)t * 16 * 128, w + (size_t)t * 16, k_idx, n, row);
+    exact_scores_block<kRowThreads, 4>(q_idx + (size_t)t * 16 * 128, w + (size_t)t * 16, k_idx, n, row);
     __syncthreads();
     row_topk(row, n, k, idx + (size_t)t * k, rsh, sh, fs);
     __syncthreads();
