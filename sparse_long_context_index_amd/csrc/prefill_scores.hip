@@ -15,6 +15,8 @@
 // carry less precision than fp32 (measured and bounded in the tests).
 //
 // Built with MFMA results in VGPRs (no accumulation-register reads).
+#include <type_traits>
+
 #include "dsa_common.hpp"
 #include "indexer.hpp"
 #include "kernels.hpp"
@@ -36,14 +38,22 @@ static_assert(kRoundKeys == 16 * 4, "a round is 16 lanes x 4 keys of one stored 
 // head sums and the causal mask.  The block's keys are kk + step * c for
 // c < 16; lane group g gets the scores of tokens g (x) and g + 4 (y) for key
 // kk + step * (lane % 16).  Blocks at or beyond Lk (the tail of the last
-// tile) compute on clamped keys; their scores are not used.
-__device__ __forceinline__ float2 gemm_block(const i32x8 (&a)[8], const float* wv, const i32x8& b, int64_t kk,
-                                             int step, int t0, int64_t Lk, int T, int col, int grp) {
+// tile) compute on clamped keys; their scores are not used.  Blocks beyond
+// every token of the wave are computed too and masked (a branch around them
+// would cost every block a wait for all its loads; there are few such
+// blocks).  The slot's next fragment is loaded (reload) once the MFMAs have
+// read the current one, so the load can reuse the slot's registers: loaded
+// into other registers, the ring of fragments would be copied back, and
+// waited for, at every round.
+template <class Reload>
+__device__ __forceinline__ float2 gemm_block(const i32x8 (&a)[8], const float* wv, i32x8& slot, Reload reload,
+                                             int64_t kk, int step, int t0, int64_t Lk, int T, int col, int grp) {
   const int64_t p0 = Lk - T + t0;                       // position of the wave's first token
-  if (kk > p0 + 7) return make_float2(-INFINITY, -INFINITY);   // every key beyond every token
+  const i32x8 b = slot;
   f32x4 c[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) c[j] = mfma_f8_16x16x128(a[j], b, f32x4{0.f, 0.f, 0.f, 0.f});
+  slot = reload();
   __builtin_amdgcn_sched_barrier(0);                    // all eight tiles in flight before the epilogue
   float x[8];
 #pragma unroll
@@ -54,7 +64,7 @@ __device__ __forceinline__ float2 gemm_block(const i32x8 (&a)[8], const float* w
   }
   float lo = sum_rows4x4(x[0], x[1], x[2], x[3]);
   float hi = sum_rows4x4(x[4], x[5], x[6], x[7]);
-  if (kk + 15 * step > p0) {                            // the block crosses the causal edge
+  if (kk + 15 * step > p0) {                            // the block reaches the causal edge (wave-uniform)
     const int64_t key = kk + (int64_t)step * col;
     if (key > p0 + grp) lo = -INFINITY;
     if (key > p0 + grp + 4) hi = -INFINITY;
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int t0 = (int)(ttile * kGemmTok) + wave * 8;
+  const int t0 = (int)(ttile * kGemmTok) + __builtin_amdgcn_readfirstlane(wave) * 8;   // wave-uniform
   const int64_t s0 = ktile * kGemmKeys;                // first key of the tile, in key-space units
   // candidate mode: the norm bounds of the tile's keys, staged in LDS once
   __shared__ float nsm[kMode == kGemmCand ? kGemmKeys : 1];
@@ -249,20 +259,14 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
     const int t = t0 + j < T ? t0 + j : T - 1;
     a[j] = load_frag32_cached(ga.q_idx + (size_t)(t * 16 + col) * 128 + 32 * grp);
   }
-  // key blocks beyond the key space are clamped into the cache
+  // key blocks beyond the key space are clamped into the cache (only the
+  // last key tile has any: it runs a copy of the loop with the clamp, so the
+  // loop body has no branch around its loads)
   const int64_t last = Lk - 1;
   const bool tail = (s0 + kGemmKeys) * step > Lk;      // wave-uniform
   const uint8_t* kp = ga.k_idx + (s0 + col) * step * 128 + 32 * grp;
-  auto load_b = [&](int kb) {
-    if (!tail) return load_frag32_cached(kp + (int64_t)kb * 16 * step * 128);
-    const int64_t key = (s0 + kb * 16 + col) * step;
-    return load_frag32_cached(ga.k_idx + (key < last ? key : last) * 128 + 32 * grp);
-  };
   constexpr int NB = kGemmKeys / 16;
   static_assert(NB % PF == 0 && PF <= kGemmPF, "whole prefetch rounds");
-  i32x8 b[PF];
-#pragma unroll
-  for (int u = 0; u < PF; ++u) b[u] = load_b(u);
   const int64_t end = ga.nkeys - s0 < kGemmKeys ? ga.nkeys - s0 : kGemmKeys;   // keys of this tile
   __shared__ __attribute__((aligned(16))) float stage[kMode == kGemmCand ? 1 : 4][8 * kStageStride];
   float* st = stage[kMode == kGemmCand ? 0 : wave];
@@ -284,17 +288,29 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
     }
   }
 
+  auto main_loop = [&](auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    auto load_b = [&](int kb) {
+      if constexpr (!kTail) {
+        return load_frag32_cached(kp + (int64_t)kb * 16 * step * 128);
+      } else {
+        const int64_t key = (s0 + kb * 16 + col) * step;
+        return load_frag32_cached(ga.k_idx + (key < last ? key : last) * 128 + 32 * grp);
+      }
+    };
+    i32x8 b[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) b[u] = load_b(u);
 #pragma unroll 1
   for (int kb = 0; kb < NB; kb += PF) {
     if ((int64_t)kb * 16 >= end) break;                // wave-uniform
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      const i32x8 cur = b[u];
       const int nb = kb + PF + u;
-      b[u] = load_b(nb < NB ? nb : NB - 1);           // unconditional: no branch around the load
-
       const int64_t kk = (s0 + (kb + u) * 16) * step;
-      const float2 v = gemm_block(a, wv, cur, kk, step, t0, Lk, T, col, grp);
+      // the next fragment of this slot is loaded unconditionally (no branch around the load)
+      const float2 v = gemm_block(a, wv, b[u], [&] { return load_b(nb < NB ? nb : NB - 1); }, kk, step, t0, Lk,
+                                  T, col, grp);
       if (kMode == kGemmCand) {
         // a key is a candidate of token t when its score reaches t's
         // threshold: masked keys score -inf, which no threshold admits, and
@@ -317,6 +333,11 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
     }
     if (kMode != kGemmCand) store_round(st, s0 + kb * 16, t0, ga.nkeys, T, ga.scores, ga.ld, col, grp);
   }
+  };
+  if (tail)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   if (kMode == kGemmCand) {
     // the lane rows' counts to LDS (one lane per row and token), then flush
     uint32_t* lc = lcnt[kMode == kGemmCand ? wave : 0];
