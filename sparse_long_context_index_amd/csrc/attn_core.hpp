@@ -43,8 +43,16 @@ struct Window {
   }
 };
 
+// Orders a wave's LDS accesses before and after this point (compiler and
+// hardware: a wave's LDS operations complete in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // NTB: threads of the workgroup (at least NW waves); waves beyond NW only take
-// part in the barriers.
+// part in the combine's barriers.
 template <int HKV, int NW, class Src, int NTB = NW * 64>
 __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, int t, int g, int c, int n_chunks,
                              int p0, int p1, float* part, char* smem) {
@@ -173,7 +181,10 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
         for (int b = 0; b < 8; ++b) o[b][i] *= al;
       }
     }
-    __syncthreads();
+    // the V staging area is the wave's own: its stores precede its reads
+    // (LDS operations of a wave complete in order), so no workgroup barrier
+    // holds this wave for the slowest wave's loads
+    wave_lds_sync();
     if (active) {
       // ---- PV: B operand = V[key(kg,e)][16*blk + col], key(kg,e) = e<4 ? 4kg+e : 12+4kg+e
 #pragma unroll
@@ -188,7 +199,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
         o[blk] = mfma_bf16_16x16x32(pl, __builtin_bit_cast(bf16x8, vb), o[blk]);
       }
     }
-    __syncthreads();
+    wave_lds_sync();                                        // this round's reads before the next round's stores
   }
 
   // ---- combine the waves of this workgroup
