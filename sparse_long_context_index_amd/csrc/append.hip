@@ -32,18 +32,6 @@ constexpr int kQPerKv = DSA_Q_HEADS / DSA_KV_HEADS;  // 16
 constexpr int kRowPieces = DSA_QK_DIM / 8;         // 16-byte pieces of a 192-dim bf16 row
 constexpr int kIdxPieces = DSA_IDX_DIM / 8;        // of a 128-dim bf16 row
 
-// fp32 -> fp8 e4m3 code, round to nearest even, saturating at +-448: from the
-// format (bias 7, 3 fraction bits, exponent field 0 subnormal in steps of 2^-9)
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.f);
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);   // code 8 is the smallest normal
-  uint32_t b = __float_as_uint(a);
-  b += 0x7FFFFu + ((b >> 20) & 1u);                 // keep 3 fraction bits, ties to even
-  const uint32_t e = (b >> 23) - 120u;              // 127 - 7
-  return sign | (e << 3) | ((b >> 20) & 7u);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Per-dim rotation table of one token: y_d = x_d C[d] + x_{pair(d)} S[d] with
@@ -60,15 +48,16 @@ __device__ __forceinline__ int pair_of(int d, int R) {
   return d < h ? d + h : (d < R ? d - h : d);
 }
 
-// threads d < ceil8(R) fill entry d: a_i = p base^(-2i/R) with i = d mod R/2
-__device__ __forceinline__ void rot_table(RotTable& rt, int64_t p, int R, double log2_base) {
+// threads d < ceil8(R) fill entry d: a_i = p f_i with i = d mod R/2, where
+// f_i = base^(-2i/R) comes from the host, computed there in float64
+__device__ __forceinline__ void rot_table(RotTable& rt, int64_t p, int R, const double* freq) {
   constexpr double kTwoPi1 = 6.283185307179586232;     // nearest double to 2 pi
   constexpr double kTwoPi2 = 2.4492935982947064e-16;   // 2 pi - kTwoPi1
   constexpr double kInvTwoPi = 0.15915494309189535;
   const int d = threadIdx.x, h = R >> 1;
   if (d < R) {
     const int i = d < h ? d : d - h;
-    const double a = (double)p * exp2(-2.0 * i / R * log2_base);
+    const double a = (double)p * freq[i];
     const double kq = rint(a * kInvTwoPi);
     const double r = fma(-kq, kTwoPi2, fma(-kq, kTwoPi1, a));
     double sn, cs;
@@ -108,10 +97,23 @@ __device__ __forceinline__ void unpack_bf16x8(float (&x)[8], const uint4& u) {
   }
 }
 
+// 8 floats -> 8 fp8 e4m3 codes, round to nearest even, saturating at +-448:
+// the values are clamped to [-448, 448] and converted by the hardware
+// (v_cvt_pk_fp8_f32, OCP e4m3), which then rounds to nearest even with
+// subnormals in steps of 2^-9; an exhaustive comparison over every finite
+// float with the rounding written out from the format (bias 7, 3 fraction
+// bits) found no difference.
 __device__ __forceinline__ uint2 pack_e4m3x8(const float (&y)[8]) {
-  uint32_t w[2] = {0u, 0u};
+  float c[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j >> 2] |= f32_to_e4m3_rne(y[j]) << (8 * (j & 3));
+  for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_fmed3f(y[j], -448.f, 448.f);
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h], c[4 * h + 1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h + 2], c[4 * h + 3], v, true);
+    w[h] = (uint32_t)v;
+  }
   return make_uint2(w[0], w[1]);
 }
 
@@ -127,7 +129,8 @@ struct AppendArgs {
   int64_t Lk;
   int T;
   int rot_idx, rot_main;
-  double log2_base;
+  double freq_idx[DSA_IDX_DIM / 2];   // base^(-2i/R) of the rotated index-head dims
+  double freq_main[DSA_QK_DIM / 2];   // base^(-2i/R) of the rotated attention-head dims
   uint8_t* q_idx_out;
   uint8_t* k_idx_cache;
   uint16_t* q_out;
@@ -176,7 +179,7 @@ __device__ __forceinline__ void append_indexer(const AppendArgs& ar, IdxShared& 
   static_assert(DSA_IDX_HEADS * kIdxPieces == kAppendNT, "one 16-byte query piece per thread");
   const int r = tid / kIdxPieces, d0 = 8 * (tid % kIdxPieces);
   const uint4 own = *reinterpret_cast<const uint4*>(ar.idx_q + ((size_t)t * DSA_IDX_HEADS + r) * DSA_IDX_DIM + d0);
-  rot_table(rt, p, ar.rot_idx, ar.log2_base);
+  rot_table(rt, p, ar.rot_idx, ar.freq_idx);
   if (tid >> 6 == kLnWave) index_key_norm(ar, sh, t);
   *reinterpret_cast<uint4*>(&sh.xq[r][d0]) = own;
   __syncthreads();
@@ -223,7 +226,7 @@ __device__ __forceinline__ void append_kv_head(const AppendArgs& ar, MainShared&
     *reinterpret_cast<uint4*>(ar.v_cache + ((size_t)p * DSA_KV_HEADS + g) * DSA_V_DIM + o) =
         *reinterpret_cast<const uint4*>(ar.v + ((size_t)t * DSA_KV_HEADS + g) * DSA_V_DIM + o);
   }
-  rot_table(rt, p, ar.rot_main, ar.log2_base);
+  rot_table(rt, p, ar.rot_main, ar.freq_main);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int c = tid + u * kAppendNT;
@@ -274,8 +277,11 @@ hipError_t launch_cache_append(const uint16_t* idx_q, const uint16_t* idx_k, con
   // the table threads (one per rotated dim) fit in the workgroup
   if (rot_idx > DSA_IDX_DIM || rot_main > DSA_QK_DIM || rot_idx < 2 || rot_main < 2 || (rot_idx | rot_main) & 1)
     return hipErrorInvalidValue;
-  AppendArgs ar{idx_q, idx_k, ln_gamma, ln_beta, ln_eps, q, k, v, Lk, T, rot_idx, rot_main, std::log2(base),
+  AppendArgs ar{idx_q, idx_k, ln_gamma, ln_beta, ln_eps, q, k, v, Lk, T, rot_idx, rot_main, {}, {},
                 q_idx_out, k_idx_cache, q_out, k_cache, v_cache};
+  const double lb = std::log2(base);
+  for (int i = 0; i < rot_idx / 2; ++i) ar.freq_idx[i] = std::exp2(-2.0 * i / rot_idx * lb);
+  for (int i = 0; i < rot_main / 2; ++i) ar.freq_main[i] = std::exp2(-2.0 * i / rot_main * lb);
   hipLaunchKernelGGL(cache_append_kernel, dim3(T, 1 + DSA_KV_HEADS), dim3(kAppendNT), 0, st, ar);
   return hipGetLastError();
 }

@@ -112,7 +112,8 @@ def check_append(out, inp, Lk, T, ln=True):
 
 
 @pytest.mark.parametrize("T,Lk", [(1, 1), (1, 8192), (4, 131072), (3, 1000), (8, 1048576), (1, 1048576),
-                                  (64, 70000), (511, 4000), (512, 512), (600, 2000), (1100, 70000)])
+                                  (64, 70000), (511, 4000), (512, 512), (600, 2000), (1100, 70000),
+                                  (1027, 5000), (2050, 9000)])
 def test_cache_append(dev, T, Lk):
     inp = synth.append_inputs(T, seed=T * 7 + Lk % 1000)
     out = run_append(dev, inp, Lk, T)
