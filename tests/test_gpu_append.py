@@ -143,6 +143,29 @@ def test_cache_append_extreme_values(dev, T):
     assert np.any((out["idx_q"] & 0x7F) == 0x7E), "no saturated fp8 code was exercised"
 
 
+def test_cache_append_every_bf16_code_to_fp8(dev):
+    # every finite bf16 code, placed in the index queries' unrotated dims,
+    # passes through the fp8 rounding unchanged by any arithmetic, so its e4m3
+    # code must equal the oracle's rounding of the same value exactly: round to
+    # nearest even, subnormals in steps of 2^-9, saturation at +-448
+    codes = np.arange(65536, dtype=np.uint32)
+    codes = codes[(codes & 0x7F80) != 0x7F80].astype(np.uint16)    # drop inf / nan
+    R = ca.rotary_dims(128)
+    per_tok = 16 * (128 - R)
+    T = -(-codes.size // per_tok)
+    inp = synth.append_inputs(T, seed=31)
+    q = inp["idx_q"].copy()
+    slots = np.zeros(T * per_tok, dtype=np.uint16)
+    slots[:codes.size] = codes
+    q[:, :, R:] = slots.reshape(T, 16, 128 - R)
+    inp["idx_q"] = q
+    Lk = 3000
+    out = run_append(dev, inp, Lk, T)
+    check_append(out, inp, Lk, T)
+    got = out["idx_q"][:, :, R:].reshape(-1)[:codes.size]
+    assert np.array_equal(got, ca.to_e4m3(oracle.decode_bf16(codes).astype(np.float64)))
+
+
 def test_cache_append_prefill_chunk_sampled(dev):
     # the full prefill chunk: 8192 new tokens onto a 1,048,576-token history;
     # the oracle checks a seeded sample of tokens, each at its own position
