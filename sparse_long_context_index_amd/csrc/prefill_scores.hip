@@ -302,37 +302,37 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < PF; ++u) b[u] = load_b(u);
 #pragma unroll 1
-  for (int kb = 0; kb < NB; kb += PF) {
-    if ((int64_t)kb * 16 >= end) break;                // wave-uniform
+    for (int kb = 0; kb < NB; kb += PF) {
+      if ((int64_t)kb * 16 >= end) break;                // wave-uniform
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int nb = kb + PF + u;
-      const int64_t kk = (s0 + (kb + u) * 16) * step;
-      // the next fragment of this slot is loaded unconditionally (no branch around the load)
-      const float2 v = gemm_block(a, wv, b[u], [&] { return load_b(nb < NB ? nb : NB - 1); }, kk, step, t0, Lk,
-                                  T, col, grp);
-      if (kMode == kGemmCand) {
-        // a key is a candidate of token t when its score reaches t's
-        // threshold: masked keys score -inf, which no threshold admits, and
-        // tokens beyond T have threshold +inf
-        const int64_t key = kk + col;
-        const float ncur = nsm[(kb + u) * 16 + col];
-        const bool ok0 = v.x + cw0 * ncur >= th0, ok1 = v.y + cw1 * ncur >= th1;
-        const uint32_t k0 = order_key(v.x), k1 = order_key(v.y);
-        const uint64_t m0 = __ballot(ok0), m1 = __ballot(ok1);
-        if (m0 | m1) {                                 // wave-uniform
-          uint2* lb = lcand[kMode == kGemmCand ? wave : 0];
-          emit_local(ok0, m0, grp, lane, c0, lb + grp * kLocalCand, t0 + grp, k0, (uint32_t)key, ga.cand);
-          emit_local(ok1, m1, grp, lane, c1, lb + (grp + 4) * kLocalCand, t0 + grp + 4, k1, (uint32_t)key,
-                     ga.cand);
+      for (int u = 0; u < PF; ++u) {
+        const int nb = kb + PF + u;
+        const int64_t kk = (s0 + (kb + u) * 16) * step;
+        // the next fragment of this slot is loaded unconditionally (no branch around the load)
+        const float2 v = gemm_block(a, wv, b[u], [&] { return load_b(nb < NB ? nb : NB - 1); }, kk, step, t0, Lk,
+                                    T, col, grp);
+        if (kMode == kGemmCand) {
+          // a key is a candidate of token t when its score reaches t's
+          // threshold: masked keys score -inf, which no threshold admits, and
+          // tokens beyond T have threshold +inf
+          const int64_t key = kk + col;
+          const float ncur = nsm[(kb + u) * 16 + col];
+          const bool ok0 = v.x + cw0 * ncur >= th0, ok1 = v.y + cw1 * ncur >= th1;
+          const uint32_t k0 = order_key(v.x), k1 = order_key(v.y);
+          const uint64_t m0 = __ballot(ok0), m1 = __ballot(ok1);
+          if (m0 | m1) {                                 // wave-uniform
+            uint2* lb = lcand[kMode == kGemmCand ? wave : 0];
+            emit_local(ok0, m0, grp, lane, c0, lb + grp * kLocalCand, t0 + grp, k0, (uint32_t)key, ga.cand);
+            emit_local(ok1, m1, grp, lane, c1, lb + (grp + 4) * kLocalCand, t0 + grp + 4, k1, (uint32_t)key,
+                       ga.cand);
+          }
+        } else {
+          st[grp * kStageStride + 16 * u + col] = v.x;
+          st[(grp + 4) * kStageStride + 16 * u + col] = v.y;
         }
-      } else {
-        st[grp * kStageStride + 16 * u + col] = v.x;
-        st[(grp + 4) * kStageStride + 16 * u + col] = v.y;
       }
+      if (kMode != kGemmCand) store_round(st, s0 + kb * 16, t0, ga.nkeys, T, ga.scores, ga.ld, col, grp);
     }
-    if (kMode != kGemmCand) store_round(st, s0 + kb * 16, t0, ga.nkeys, T, ga.scores, ga.ld, col, grp);
-  }
   };
   if (tail)
     main_loop(std::true_type{});
