@@ -20,15 +20,18 @@ struct AttnSmem {
   static constexpr int bytes = stage > merge ? stage : merge;
 };
 
-// list position -> cache row, or -1 for an empty slot
+// List position p -> cache row, or -1 for an empty slot (p >= p1 included).
+// The position is clamped into the list and its entry always read, then
+// masked: a read under a branch would be waited for inside the branch, so
+// the reads of a tile would run one after another instead of together.
 struct IdxList {
   const int32_t* row_idx;   // idx[t] row
-  int len;
+  int len;                  // >= 1
   int64_t n_rows;
-  __device__ int64_t row(int p) const {
-    if (p >= len) return -1;
-    const int32_t j = row_idx[p];
-    return (j >= 0 && (int64_t)j < n_rows) ? (int64_t)j : -1;
+  __device__ int64_t row(int p, int p1) const {
+    const int32_t j = row_idx[p < len ? p : len - 1];
+    const bool ok = (p < p1) & (p < len) & (j >= 0) & ((int64_t)j < n_rows);   // no short-circuit branch
+    return ok ? (int64_t)j : -1;
   }
 };
 
@@ -36,10 +39,10 @@ struct Window {
   int64_t first;            // cache row of list position 0
   int len;
   int64_t n_rows;
-  __device__ int64_t row(int p) const {
-    if (p >= len) return -1;
+  __device__ int64_t row(int p, int p1) const {
     const int64_t r = first + p;
-    return (r >= 0 && r < n_rows) ? r : -1;
+    const bool ok = (p < p1) & (p < len) & (r >= 0) & (r < n_rows);
+    return ok ? r : -1;
   }
 };
 
@@ -67,18 +70,16 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
 
   // Q as the B operand: column = head; k-step s, k-group kg covers dims
   // 32 s + 8 kg .. + 7 (K uses the same order, so the 4 k-groups of a key row
-  // read 64 contiguous bytes per load)
+  // read 64 contiguous bytes per load).  With fewer than 16 query heads per KV
+  // head (GH = 8) columns GH .. 15 repeat real heads: their logits, weights
+  // and output rows are never combined or written, and no value is masked, so
+  // nothing waits for these loads before the K/V loads are issued.
   bf16x8 qf[6];
   {
-    const bool hv = col < GH;
-    const int h = g * GH + (hv ? col : 0);
+    const int h = g * GH + (col % GH);
     const uint16_t* qp = a.q + ((size_t)t * 64 + h) * 192 + 8 * kg;
 #pragma unroll
-    for (int s = 0; s < 6; ++s) {
-      u16x8 raw = *reinterpret_cast<const u16x8*>(qp + 32 * s);
-      if (!hv) raw = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int s = 0; s < 6; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + 32 * s));
   }
 
   f32x4 o[8];
@@ -104,14 +105,12 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       int64_t rk[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int p = tb + b * 16 + col;
-        rk[b] = p < p1 ? src.row(p) : -1;
+        rk[b] = src.row(tb + b * 16 + col, p1);
       }
       int64_t rv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int p = tb + 4 * i + (lane >> 4);
-        rv[i] = p < p1 ? src.row(p) : -1;
+        rv[i] = src.row(tb + 4 * i + (lane >> 4), p1);
       }
       u16x8 kraw[2][6];
 #pragma unroll

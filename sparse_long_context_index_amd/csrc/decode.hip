@@ -133,12 +133,15 @@ __device__ __forceinline__ void reduce_lists(uint32_t& n, uint32_t& f, uint32_t&
   }
 }
 
+// the kept list in LDS (DSA_TOPK_MAX entries; positions at or past p1 are
+// read clamped and masked, see IdxList)
 struct LdsList {
   const int32_t* sel;
   int64_t n_rows;
-  __device__ int64_t row(int p) const {
-    const int32_t j = sel[p];
-    return (j >= 0 && (int64_t)j < n_rows) ? (int64_t)j : -1;
+  __device__ int64_t row(int p, int p1) const {
+    const int32_t j = sel[p < DSA_TOPK_MAX ? p : DSA_TOPK_MAX - 1];
+    const bool ok = (p < p1) & (j >= 0) & ((int64_t)j < n_rows);   // no short-circuit branch
+    return ok ? (int64_t)j : -1;
   }
 };
 
