@@ -47,11 +47,19 @@ __global__ __launch_bounds__(NW * 64) void swa_attn_kernel(AttnArgs a, int n_chu
                                                           float* part) {
   __shared__ __attribute__((aligned(16))) char smem[AttnSmem<NW>::bytes];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int64_t n = a.seq_len[b];
+  const int64_t s = a.seq_start[b];              // issued first: both scalar loads are in flight before
+  const int64_t n = a.seq_len[b];                // the wait that the first use of either needs
   const int len = n <= 0 ? 0 : (int)(n < a.window ? n : a.window);
-  Window src{a.seq_start[b] + n - len, len, a.n_rows};
+  const int64_t first = s + n - len;
+  // Positions whose rows lie at or past the cache's end read as empty slots
+  // either way; leaving them out of the range also makes the loop bound need
+  // both descriptor words, so both loads leave before the first branch (one
+  // round trip before the K/V addresses are known, not two).
+  const int64_t room = a.n_rows - first;
+  const int lenc = room < (int64_t)len ? (room > 0 ? (int)room : 0) : len;
+  Window src{first, len, a.n_rows};
   const int p0 = c * chunk_keys;
-  const int p1 = p0 + chunk_keys < len ? p0 + chunk_keys : len;
+  const int p1 = p0 + chunk_keys < lenc ? p0 + chunk_keys : lenc;
   attend_chunk<HKV, NW>(a, src, b, g, c, n_chunks, p0 < p1 ? p0 : p1, p1, part, smem);
 }
 

@@ -81,6 +81,20 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
 #pragma unroll
     for (int s = 0; s < 6; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + 32 * s));
   }
+  // The combine's thread layout (see below) and, for a unit in one chunk, the
+  // sink logits of the heads this thread writes, loaded now with the queries
+  // (read after the combine they would add a round trip at the very end).
+  // Without a sink the loads read the query instead and are discarded.
+  constexpr int R = NW * 64 / 128;             // heads covered per pass
+  constexpr int Q = GH / R;                    // passes
+  static_assert(NW * 64 % 128 == 0 && GH % R == 0, "combine layout");
+  const int h0 = (threadIdx.x >> 7) & (R - 1);
+  float sinkv[Q];
+  {
+    const float* sp = a.sink ? a.sink + g * GH + h0 : reinterpret_cast<const float*>(a.q);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) sinkv[q] = sp[R * q];
+  }
 
   f32x4 o[8];
 #pragma unroll
@@ -224,11 +238,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
   // every thread combines outputs (head hc, dim dv) for hc = h0 + R*q; all
   // LDS reads are issued before any result is written
   const int unit = t * HKV + g;
-  constexpr int R = NW * 64 / 128;             // heads covered per pass
-  constexpr int Q = GH / R;                    // passes
-  static_assert(NW * 64 % 128 == 0 && GH % R == 0, "combine layout");
   const int dv = threadIdx.x & 127;
-  const int h0 = threadIdx.x >> 7;
   float Mq[Q], Lq[Q], Oq[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
@@ -262,7 +272,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       float Mf = M;
       float sl = 0.f;
       if (a.sink) {
-        const float s2 = a.sink[h] * kLog2e;
+        const float s2 = sinkv[q] * kLog2e;
         Mf = fmaxf(M, s2);
         sl = exp2f(s2 - Mf);
       }
