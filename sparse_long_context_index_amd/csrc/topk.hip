@@ -23,7 +23,8 @@
 //                           block of the row resolves tau and emits the row.
 //  * Many rows (prefill), and rows too short for the multi-block path:
 //    topk_row_kernel, one 1024-thread workgroup per row, candidates in LDS
-//    (a row of up to 16,384 keys is held in LDS whole).
+//    (a row of up to 16,384 keys is held in LDS whole, one of up to 65,536
+//    keys in registers).
 // A candidate slot that overflows switches the row's final pass to reading
 // the scores row itself (same result, slower).
 #include "dsa_common.hpp"
@@ -473,10 +474,151 @@ __device__ void short_row_select(const float* __restrict__ row, int n, int k, ui
   bitmap_emit<NT>(bm, nw, scan_sm, k, out_row);
 }
 
+// Rows of kSmallRow < n <= kRegRow keys: each thread keeps its kRegPer keys
+// (elements e * NT + thread) in registers, so the row is read once and every
+// pass after it runs on registers and LDS.
+//   1. a lower bound L0 of the threshold: with c = ceil(k / NT), every thread
+//      holds c keys at or above its own c-th largest, so the smallest of those
+//      c-th largest keys has at least c * NT >= k keys at or above it;
+//   2. a histogram of the keys >= L0 over [L0, max] in 4,096 bins (the range
+//      adapts to the row, so the keys spread over the bins instead of piling
+//      into the few that a fixed digit gives them), and the bin b1 that holds
+//      the k-th key;
+//   3. when b1 holds few keys, they are collected and ranked directly by (key
+//      desc, index asc): the k-th key (tk, ti) of the row is the one of rank
+//      k - (keys above the bin) - 1;
+//   4. the kept keys (key > tk, or key == tk and index <= ti) are marked in a
+//      bitmap by wave ballots and emitted in index order.
+// A crowded threshold bin (ties, narrow rows) returns false without output;
+// the caller then takes the general path.
+constexpr int kRegPer = 64;
+constexpr int kRegRow = kRegPer * kRowThreads;
+constexpr int kBinCap = 256;                       // threshold-bin keys ranked directly
+static_assert(kSmallRow >= 2 * kRowThreads && DSA_TOPK_MAX <= 2 * kRowThreads, "threshold bound of step 1");
+
+struct RegRowShared {
+  uint32_t hist[kHistBins];
+  uint64_t bm[kRegRow / 64];                       // kept-key bitmap, bit s % 64 of word s / 64
+  alignas(16) uint32_t ck[kBinCap];                // keys of the threshold bin
+  alignas(16) uint32_t ci[kBinCap];                // and their indices
+  uint32_t red[4 * kRowWaves];
+  uint32_t bscan[kRowWaves], bout[3];
+  uint32_t escan[kRowWaves];
+  uint32_t n1, tk, ti;
+};
+
+template <int NT>
+__device__ bool reg_row_select(const float* __restrict__ row, int n, int k, RegRowShared& g,
+                               int32_t* __restrict__ out_row) {
+  constexpr int E = kRegPer;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // ---- the keys: every load in flight at once (positions past the row read
+  // its last score and are masked to key 0, which no score maps to)
+  uint32_t key[E];
+  {
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int s = e * NT + tid;
+      v[e] = row[s < n ? s : n - 1];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = e * NT + tid < n ? order_key(v[e]) : 0u;
+  }
+  // ---- 1. the largest key, and each thread's c-th largest (c <= 2)
+  const int c = (k + NT - 1) / NT;
+  uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t lo = m1 < key[e] ? m1 : key[e];
+    m1 = m1 > key[e] ? m1 : key[e];
+    m2 = m2 > lo ? m2 : lo;
+  }
+  const int cnt = tid < n ? (n - 1 - tid) / NT + 1 : 0;      // this thread's keys
+  uint32_t kmax = m1, L0 = cnt >= c ? (c == 1 ? m1 : m2) : 0xFFFFFFFFu, unused = 0xFFFFFFFFu;
+  uint32_t nc = cnt >= c ? 1u : 0u;
+  for (int i = tid; i < kHistBins; i += NT) g.hist[i] = 0u;
+  if (tid == 0) g.n1 = 0u;
+  block_reduce_mmms<NT>(kmax, L0, unused, nc, g.red);
+  if ((uint64_t)nc * (uint32_t)c < (uint64_t)k) L0 = 1u;     // not reached for n > kSmallRow; every key counts
+  // ---- 2. histogram of the keys >= L0 over [L0, kmax]
+  const uint32_t span = kmax - L0;
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  const int s1 = bits > 12 ? bits - 12 : 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (key[e] >= L0) atomicAdd(&g.hist[(key[e] - L0) >> s1], 1u);
+  __syncthreads();
+  uint32_t b1, above1, cnt1;
+  find_threshold_bin_once<NT, kHistBins>(g.hist, (uint32_t)k, g.bscan, g.bout, &b1, &above1, &cnt1);
+  if (cnt1 > (uint32_t)kBinCap) {                  // block-uniform
+    __syncthreads();                               // the caller reuses this memory
+    return false;
+  }
+  const uint32_t need = (uint32_t)k - above1;     // 1 <= need <= cnt1
+  const uint32_t lo = L0 + (b1 << s1);
+  const uint32_t wid = (1u << s1) - 1u;
+  const uint32_t hi = lo > 0xFFFFFFFFu - wid ? 0xFFFFFFFFu : lo + wid;
+  // ---- 3. collect the bin's keys (padded to 16 with key 0, which ranks last) and rank them
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((key[e] >= lo) & (key[e] <= hi)) {
+      const uint32_t p = atomicAdd(&g.n1, 1u);
+      g.ck[p] = key[e];
+      g.ci[p] = (uint32_t)(e * NT + tid);
+    }
+  const uint32_t ncp = (cnt1 + 15u) & ~15u;
+  if ((uint32_t)tid >= cnt1 && (uint32_t)tid < ncp) {
+    g.ck[tid] = 0u;
+    g.ci[tid] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  if ((uint32_t)tid < cnt1) {
+    const uint32_t kt = g.ck[tid], it = g.ci[tid];
+    auto before = [&](uint32_t kj, uint32_t ij) {
+      return (uint32_t)(kj > kt) | ((uint32_t)(kj == kt) & (uint32_t)(ij < it));
+    };
+    uint32_t rank = 0;
+    for (uint32_t j0 = 0; j0 < ncp; j0 += 16) {
+      uint4 k4[4], i4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        k4[q] = *reinterpret_cast<const uint4*>(&g.ck[j0 + 4 * q]);
+        i4[q] = *reinterpret_cast<const uint4*>(&g.ci[j0 + 4 * q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        rank += before(k4[q].x, i4[q].x) + before(k4[q].y, i4[q].y) + before(k4[q].z, i4[q].z) +
+                before(k4[q].w, i4[q].w);
+    }
+    if (rank == need - 1u) {
+      g.tk = kt;
+      g.ti = it;
+    }
+  }
+  __syncthreads();
+  const uint32_t tk = g.tk, ti = g.ti;
+  // ---- 4. bitmap of the kept keys: the ballot of element e covers keys
+  // e * NT + 64 * wave .. + 63, one 64-bit word; lane e keeps it and every
+  // lane stores one word
+  uint64_t mine = 0ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t s = (uint32_t)(e * NT + tid);
+    const uint64_t m = __ballot((key[e] > tk) | ((key[e] == tk) & (s <= ti)));
+    mine = lane == e ? m : mine;
+  }
+  g.bm[lane * (NT / 64) + wv] = mine;
+  __syncthreads();
+  bitmap_emit<NT>(reinterpret_cast<const uint32_t*>(g.bm), (n + 31) / 32, g.escan, k, out_row);
+  return true;
+}
+
 union RowShared {
   uint32_t rep[kRowReps * kRepStride];
   static_assert(kRowReps * kRepStride >= kSmallRow, "a short row's keys fit the level-1 copies' space");
   RowCand c;
+  RegRowShared g;
 };
 
 struct RowSel {
@@ -488,6 +630,9 @@ struct RowSel {
 
 // The top-k of one scores row of n visible keys into out_row[0 .. k), by the
 // kRowThreads threads of a workgroup (the shared structures are the caller's).
+// kRegRows: rows of up to kRegRow keys take the register-resident selection
+// (a kernel whose other work needs the registers leaves it out).
+template <bool kRegRows>
 __device__ __forceinline__ void row_topk(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out_row,
                          RowShared& rsh, RowSel& sh, FinalShared& fs) {
   const int lane = threadIdx.x & 63;
@@ -497,6 +642,8 @@ __device__ __forceinline__ void row_topk(const float* __restrict__ row, int64_t 
     for (int j = threadIdx.x; j < k; j += kRowThreads) out_row[j] = j < n ? j : -1;
   } else if (n <= (int64_t)kSmallRow) {
     short_row_select<kRowThreads>(row, (int)n, k, rsh.rep, sh.rs, sh.sel, fs.scan, out_row);
+  } else if (kRegRows && n <= (int64_t)kRegRow && reg_row_select<kRowThreads>(row, (int)n, k, rsh.g, out_row)) {
+    // done
   } else {
     // ---- level-1 histogram
     static_assert((kRowReps * kRepStride) % 4 == 0, "16-byte clears");
@@ -653,7 +800,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   int64_t n = Lk - T + tt + 1;
   n = n > 0 ? n : 0;
   int32_t* out_row = idx + (size_t)t * k;
-  row_topk(scores + (int64_t)t * ld, n, k, out_row, rsh, sh, fs);
+  row_topk<true>(scores + (int64_t)t * ld, n, k, out_row, rsh, sh, fs);
   if (idx_rows) {
     // the same set as cache rows of the sequence
     __syncthreads();
@@ -685,7 +832,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_fallback_kernel(
     const int64_t n = Lk - T + (int64_t)t + 1;
     exact_scores_block<kRowThreads, 4>(q_idx + (size_t)t * 16 * 128, w + (size_t)t * 16, k_idx, n, row);
     __syncthreads();
-    row_topk(row, n, k, idx + (size_t)t * k, rsh, sh, fs);
+    row_topk<false>(row, n, k, idx + (size_t)t * k, rsh, sh, fs);
     __syncthreads();
   }
 }

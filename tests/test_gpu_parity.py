@@ -211,6 +211,11 @@ def topk_ref_exact(S, Lk, T, k):
     (17, 5000, 2048, "normal"), (40, 33000, 2048, "ties"), (20, 3000, 2048, "allequal"),
     (24, 20000, 64, "planted"), (32, 100, 2048, "normal"),
     (3, 16386, 1000, "ties"), (1, 16384, 2048, "allequal"), (2, 16385, 2048, "negative"),
+    # one workgroup per row with the row in registers (16,384 < keys <= 65,536),
+    # and the rows just past it
+    (12, 65536, 2048, "normal"), (9, 65536, 1024, "normal"), (10, 65536, 1025, "planted"),
+    (9, 40000, 2048, "wide"), (9, 30000, 2048, "negative"), (16, 65536, 2048, "zeros"),
+    (9, 16400, 1, "normal"), (9, 65536, 7, "ties"), (9, 65540, 2048, "normal"), (9, 50000, 2048, "allequal"),
 ])
 def test_topk_bit_exact(dev, T, Lk, k, kind):
     rng = np.random.default_rng(zlib.crc32(repr((T, Lk, k, kind)).encode()))
