@@ -229,9 +229,10 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     if (sb.spread) {
       // Workgroups dealt by length: every workgroup derives the same deal from
       // the lengths -- sequence i (ng_i key groups of N in all) gets 1 +
-      // floor(768 ng_i / N) workgroups, at most ng_i, in sequence order --
-      // and takes its place in it; the grid has 768 + B workgroups, enough for
-      // any deal.  Grid dimension y is 1.
+      // floor((768 - B) ng_i / N) workgroups, at most ng_i, in sequence order
+      // -- and takes its place in it.  The deal uses at most 768 workgroups,
+      // the number that runs at once (3 per CU), so none waits for a slot;
+      // the grid has 768 + B, and the spares exit.  Grid dimension y is 1.
       __shared__ uint32_t deal_sm[4];
       __shared__ int64_t deal_out[3];
       int64_t f0;
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       (void)block_excl_scan<256>(ng, deal_sm, &N);
       uint32_t per = 0;
       if (ng) {
-        per = 1u + (uint32_t)((uint64_t)kPlainScanBlocks * ng / N);
+        per = 1u + (uint32_t)((uint64_t)(kPlainScanBlocks - sb.spread) * ng / N);
         per = per < ng ? per : ng;
       }
       const uint32_t ex = block_excl_scan<256>(per, deal_sm, &used);
