@@ -146,3 +146,13 @@ def test_decode_batch_many_sequences(dev):
     o, idx, _ = run_batch(dev, seqs, 1, 256, seed=9)
     for b in (0, 1, 150, int(np.argmax(lens)), 299):
         check_seq(dev, seqs[b], 1, 256, o[b], idx[b], seqs[0]["sink"])
+
+
+def test_decode_batch_256_sequences(dev):
+    # the most sequences the length deal serves (256): at most 768 workgroups
+    # are dealt, at least one per sequence
+    lens = [int(n) for n in np.random.default_rng(11).integers(1, 20000, size=256)]
+    seqs = synth.batch_inputs(lens, 1, 256, seed=11)
+    o, idx, _ = run_batch(dev, seqs, 1, 256, seed=11)
+    for b in (0, 7, 128, int(np.argmax(lens)), int(np.argmin(lens)), 255):
+        check_seq(dev, seqs[b], 1, 256, o[b], idx[b], seqs[0]["sink"])
