@@ -46,7 +46,6 @@ struct DecodeLayout {
   size_t scores, idx, topk, attn, lkeys, lidx, lcount, part, total;
 };
 
-constexpr int kScanListTMax = 4;                // rows the fused list path serves
 constexpr size_t kScanListLdsMax = 80 * 1024;   // keeps two scan workgroups per CU
 constexpr int kScanListsMax = 512;
 

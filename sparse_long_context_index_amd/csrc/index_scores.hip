@@ -513,19 +513,26 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const bool with_lists = lists.keys != nullptr;
+    if (with_lists && T > kScanListTMax) return hipErrorInvalidValue;
     switch (T) {
+#define DSA_SCAN_PLAIN(n)                                                                                   \
+  hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w, k_idx, Lk, \
+                     scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{})
 #define DSA_SCAN_CASE(n)                                                                                    \
   case n:                                                                                                   \
     if (with_lists)                                                                                         \
       hipLaunchKernelGGL((idx_scan_kernel<n, true>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,    \
                          k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});                \
     else                                                                                                    \
-      hipLaunchKernelGGL((idx_scan_kernel<n, false>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,   \
-                         k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});                \
+      DSA_SCAN_PLAIN(n);                                                                                    \
     break;
       DSA_SCAN_CASE(1) DSA_SCAN_CASE(2) DSA_SCAN_CASE(3) DSA_SCAN_CASE(4)
-      DSA_SCAN_CASE(5) DSA_SCAN_CASE(6) DSA_SCAN_CASE(7) DSA_SCAN_CASE(8)
+      case 5: DSA_SCAN_PLAIN(5); break;
+      case 6: DSA_SCAN_PLAIN(6); break;
+      case 7: DSA_SCAN_PLAIN(7); break;
+      case 8: DSA_SCAN_PLAIN(8); break;
 #undef DSA_SCAN_CASE
+#undef DSA_SCAN_PLAIN
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

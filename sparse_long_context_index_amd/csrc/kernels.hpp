@@ -12,6 +12,7 @@ constexpr int kScanHistTMax = 4;          // the scan also builds the top-k hist
 constexpr int kTopkMultiRowsMax = 8;      // rows handled by the multi-block top-k
 
 constexpr int kListM = 32;                // per-workgroup local top list of the decode scan
+constexpr int kScanListTMax = 4;          // query rows the list scan (and the fused decode step) serves
 
 // A batch of ragged sequences over shared caches: sequence b owns cache rows
 // start[b] .. start[b] + len[b] - 1 (its history and its T new tokens).  A
