@@ -28,6 +28,7 @@ OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_ATTN, OP_SWA_ATTN, OP_DECODE_STEP, OP_PREFIL
     OP_INDEX_RECALL = range(8)
 
 IDX_HEADS, IDX_DIM, Q_HEADS, QK_DIM, V_DIM = 16, 128, 64, 192, 128
+KV_HEADS, SWA_KV_HEADS = 4, 8
 ROPE_BASE = 1.0e7          # DSA_ROPE_BASE
 ROT_IDX, ROT_MAIN = 42, 64  # a third of the 128- and 192-dim heads
 DSA_KV_HEADS, SWA_KV_HEADS, TOPK_MAX, DECODE_T_MAX = 4, 8, 2048, 8
@@ -88,14 +89,23 @@ def _check(status: int, what: str):
         raise DsaError(f"{what}: {msg}")
 
 
-def _dev(t: Optional[torch.Tensor], name: str):
+def _dev(t: Optional[torch.Tensor], name: str, need: int = 0):
+    """Device pointer of t; need: the bytes the call reads or writes there
+    (the C interface takes no buffer sizes, so a short buffer is refused here)."""
     if t is None:
         return None
     if not t.is_cuda:
         raise DsaError(f"{name} must be a GPU tensor (got device {t.device})")
     if not t.is_contiguous():
         raise DsaError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < need:
+        raise DsaError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {need}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(T: int, ld: int, n: int, item: int = 4) -> int:
+    """bytes of T rows of n items at stride ld"""
+    return ((T - 1) * ld + n) * item if T > 0 and n > 0 else 0
 
 
 def _stream():
@@ -137,8 +147,9 @@ def dsa_index_scores(q_idx, w, k_idx, Lk: int, T: int, scores=None, ld: Optional
     if scores is None:
         scores = torch.empty((T, Lk), dtype=torch.float32, device=q_idx.device)
     ld = scores.shape[-1] if ld is None else ld
-    _check(load().dsa_index_scores(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), Lk, T,
-                                   _dev(scores, "scores"), ld, _stream()), "dsa_index_scores")
+    _check(load().dsa_index_scores(_dev(q_idx, "q_idx", T * IDX_HEADS * IDX_DIM), _dev(w, "w", T * IDX_HEADS * 4),
+                                   _dev(k_idx, "k_idx", Lk * IDX_DIM), Lk, T,
+                                   _dev(scores, "scores", _rows(T, ld, Lk)), ld, _stream()), "dsa_index_scores")
     return scores
 
 
@@ -148,8 +159,8 @@ def dsa_topk(scores, Lk: int, T: int, k: int, idx=None, ws: Optional[Workspace] 
     if idx is None:
         idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     ws = (ws or Workspace(device=scores.device)).ensure(workspace_bytes(OP_TOPK, Lk, T, k))
-    _check(load().dsa_topk(_dev(scores, "scores"), ld, Lk, T, k, _dev(idx, "idx"), ws.ptr, ws.nbytes,
-                           _stream()), "dsa_topk")
+    _check(load().dsa_topk(_dev(scores, "scores", _rows(T, ld, Lk)), ld, Lk, T, k, _dev(idx, "idx", T * k * 4),
+                           ws.ptr, ws.nbytes, _stream()), "dsa_topk")
     return idx
 
 
@@ -161,11 +172,16 @@ def dsa_decode_batch(q_idx, w, k_idx, q, k_cache, v_cache, seq_start, seq_len, m
     if out is None:
         out = torch.empty((B, T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
     ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_DECODE_BATCH, max_len, T, k, B))
-    _check(load().dsa_decode_batch(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
-                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), n_rows,
-                                   _dev(seq_start, "seq_start"), _dev(seq_len, "seq_len"), B, T, max_len, k,
-                                   _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
-                                   _dev(idx_out, "idx_out"), ws.ptr, ws.nbytes, _stream()), "dsa_decode_batch")
+    R = B * T
+    _check(load().dsa_decode_batch(_dev(q_idx, "q_idx", R * IDX_HEADS * IDX_DIM), _dev(w, "w", R * IDX_HEADS * 4),
+                                   _dev(k_idx, "k_idx", n_rows * IDX_DIM), _dev(q, "q", R * Q_HEADS * QK_DIM * 2),
+                                   _dev(k_cache, "k_cache", n_rows * KV_HEADS * QK_DIM * 2),
+                                   _dev(v_cache, "v_cache", n_rows * KV_HEADS * V_DIM * 2), n_rows,
+                                   _dev(seq_start, "seq_start", B * 8), _dev(seq_len, "seq_len", B * 4), B, T,
+                                   max_len, k, _dev(sink, "sink", Q_HEADS * 4), float(sm_scale),
+                                   _dev(out, "out", R * Q_HEADS * V_DIM * 2), _dev(lse, "lse", R * Q_HEADS * 4),
+                                   _dev(idx_out, "idx_out", R * k * 4), ws.ptr, ws.nbytes, _stream()),
+           "dsa_decode_batch")
     return out
 
 
@@ -176,9 +192,12 @@ def dsa_index_recall(q, k_cache, v_cache, Lk: int, idx, sm_scale: float, recall=
     if recall is None:
         recall = torch.empty((T, Q_HEADS), dtype=torch.float32, device=q.device)
     ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_INDEX_RECALL, Lk, T, k))
-    _check(load().dsa_index_recall(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk,
-                                   _dev(idx, "idx"), T, k, float(sm_scale), _dev(recall, "recall"),
-                                   _dev(lse_dense, "lse_dense"), ws.ptr, ws.nbytes, _stream()), "dsa_index_recall")
+    _check(load().dsa_index_recall(_dev(q, "q", T * Q_HEADS * QK_DIM * 2),
+                                   _dev(k_cache, "k_cache", Lk * KV_HEADS * QK_DIM * 2),
+                                   _dev(v_cache, "v_cache", Lk * KV_HEADS * V_DIM * 2), Lk,
+                                   _dev(idx, "idx", T * k * 4), T, k, float(sm_scale),
+                                   _dev(recall, "recall", T * Q_HEADS * 4), _dev(lse_dense, "lse_dense", T * Q_HEADS * 4),
+                                   ws.ptr, ws.nbytes, _stream()), "dsa_index_recall")
     return recall
 
 
@@ -187,8 +206,9 @@ def dsa_prefill_topk(q_idx, w, k_idx, Lk: int, T: int, k: int, idx=None, ws: Opt
     if idx is None:
         idx = torch.empty((T, k), dtype=torch.int32, device=q_idx.device)
     ws = (ws or Workspace(device=q_idx.device)).ensure(workspace_bytes(OP_PREFILL_TOPK, Lk, T, k))
-    _check(load().dsa_prefill_topk(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), Lk, T, k,
-                                   _dev(idx, "idx"), ws.ptr, ws.nbytes, _stream()), "dsa_prefill_topk")
+    _check(load().dsa_prefill_topk(_dev(q_idx, "q_idx", T * IDX_HEADS * IDX_DIM), _dev(w, "w", T * IDX_HEADS * 4),
+                                   _dev(k_idx, "k_idx", Lk * IDX_DIM), Lk, T, k, _dev(idx, "idx", T * k * 4),
+                                   ws.ptr, ws.nbytes, _stream()), "dsa_prefill_topk")
     return idx
 
 
@@ -198,9 +218,12 @@ def sparse_gqa_attn(q, k_cache, v_cache, Lk: int, idx, sink, sm_scale: float, ou
     if out is None:
         out = torch.empty((T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
     ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_SPARSE_ATTN, Lk, T, k))
-    _check(load().sparse_gqa_attn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk,
-                                  _dev(idx, "idx"), T, k, _dev(sink, "sink"), float(sm_scale),
-                                  _dev(out, "out"), _dev(lse, "lse"), ws.ptr, ws.nbytes, _stream()),
+    _check(load().sparse_gqa_attn(_dev(q, "q", T * Q_HEADS * QK_DIM * 2),
+                                  _dev(k_cache, "k_cache", Lk * KV_HEADS * QK_DIM * 2),
+                                  _dev(v_cache, "v_cache", Lk * KV_HEADS * V_DIM * 2), Lk,
+                                  _dev(idx, "idx", T * k * 4), T, k, _dev(sink, "sink", Q_HEADS * 4), float(sm_scale),
+                                  _dev(out, "out", T * Q_HEADS * V_DIM * 2), _dev(lse, "lse", T * Q_HEADS * 4),
+                                  ws.ptr, ws.nbytes, _stream()),
            "sparse_gqa_attn")
     return out
 
@@ -211,9 +234,13 @@ def swa_attn(q, k_cache, v_cache, seq_start, seq_len, window: int, sink, sm_scal
     if out is None:
         out = torch.empty((B, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
     ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_SWA_ATTN, B=B))
-    _check(load().swa_attn(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                           k_cache.shape[0], _dev(seq_start, "seq_start"), _dev(seq_len, "seq_len"), B,
-                           window, _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
+    n_rows = k_cache.shape[0]
+    _check(load().swa_attn(_dev(q, "q", B * Q_HEADS * QK_DIM * 2),
+                           _dev(k_cache, "k_cache", n_rows * SWA_KV_HEADS * QK_DIM * 2),
+                           _dev(v_cache, "v_cache", n_rows * SWA_KV_HEADS * V_DIM * 2), n_rows,
+                           _dev(seq_start, "seq_start", B * 8), _dev(seq_len, "seq_len", B * 4), B,
+                           window, _dev(sink, "sink", Q_HEADS * 4), float(sm_scale),
+                           _dev(out, "out", B * Q_HEADS * V_DIM * 2), _dev(lse, "lse", B * Q_HEADS * 4),
                            ws.ptr, ws.nbytes, _stream()), "swa_attn")
     return out
 
@@ -223,26 +250,28 @@ def dsa_decode_step(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: in
                     ws: Optional[Workspace] = None):
     if out is None:
         out = torch.empty((T, Q_HEADS, V_DIM), dtype=torch.bfloat16, device=q.device)
-    ld = scores_out.shape[-1] if scores_out is not None else 0
     ws = (ws or Workspace(device=q.device)).ensure(workspace_bytes(OP_DECODE_STEP, Lk, T, k))
-    _check(load().dsa_decode_step(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
-                                  _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk, T, k,
-                                  _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
-                                  _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld,
-                                  ws.ptr, ws.nbytes, _stream()), "dsa_decode_step")
+    args = _step_args(q_idx, w, k_idx, q, k_cache, v_cache, Lk, T, k, sink, sm_scale, out, lse, idx_out, scores_out)
+    _check(load().dsa_decode_step(*args, ws.ptr, ws.nbytes, _stream()), "dsa_decode_step")
     return out
+
+
+def _step_args(q_idx, w, k_idx, q, k_cache, v_cache, Lk, T, k, sink, sm_scale, out, lse, idx_out, scores_out):
+    ld = scores_out.shape[-1] if scores_out is not None else 0
+    return (_dev(q_idx, "q_idx", T * IDX_HEADS * IDX_DIM), _dev(w, "w", T * IDX_HEADS * 4),
+            _dev(k_idx, "k_idx", Lk * IDX_DIM), _dev(q, "q", T * Q_HEADS * QK_DIM * 2),
+            _dev(k_cache, "k_cache", Lk * KV_HEADS * QK_DIM * 2), _dev(v_cache, "v_cache", Lk * KV_HEADS * V_DIM * 2),
+            Lk, T, k, _dev(sink, "sink", Q_HEADS * 4), float(sm_scale), _dev(out, "out", T * Q_HEADS * V_DIM * 2),
+            _dev(lse, "lse", T * Q_HEADS * 4), _dev(idx_out, "idx_out", T * k * 4),
+            _dev(scores_out, "scores_out", _rows(T, ld, Lk)), ld)
 
 
 def dsa_decode_step_noalloc(q_idx, w, k_idx, q, k_cache, v_cache, Lk: int, T: int, k: int, sink,
                             sm_scale: float, out, lse=None, idx_out=None, scores_out=None):
     """dsa_decode_step on the library's static per-GPU scratch: no workspace,
     and the C call allocates nothing (the caller passes every output)."""
-    ld = scores_out.shape[-1] if scores_out is not None else 0
-    _check(load().dsa_decode_step_noalloc(_dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"), _dev(q, "q"),
-                                          _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), Lk, T, k,
-                                          _dev(sink, "sink"), float(sm_scale), _dev(out, "out"), _dev(lse, "lse"),
-                                          _dev(idx_out, "idx_out"), _dev(scores_out, "scores_out"), ld, _stream()),
-           "dsa_decode_step_noalloc")
+    args = _step_args(q_idx, w, k_idx, q, k_cache, v_cache, Lk, T, k, sink, sm_scale, out, lse, idx_out, scores_out)
+    _check(load().dsa_decode_step_noalloc(*args, _stream()), "dsa_decode_step_noalloc")
     return out
 
 
@@ -256,9 +285,13 @@ def dsa_cache_append(idx_q, idx_k, q, k, v, Lk: int, T: int, k_idx_cache, k_cach
         q_idx_out = torch.empty((T, IDX_HEADS, IDX_DIM), dtype=torch.uint8, device=dev)
     if q_out is None:
         q_out = torch.empty((T, Q_HEADS, QK_DIM), dtype=torch.bfloat16, device=dev)
-    _check(load().dsa_cache_append(_dev(idx_q, "idx_q"), _dev(idx_k, "idx_k"), _dev(ln_gamma, "ln_gamma"),
-                                   _dev(ln_beta, "ln_beta"), ln_eps, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                   Lk, T, rot_idx, rot_main, rope_base, _dev(q_idx_out, "q_idx_out"),
-                                   _dev(k_idx_cache, "k_idx_cache"), _dev(q_out, "q_out"), _dev(k_cache, "k_cache"),
-                                   _dev(v_cache, "v_cache"), _stream()), "dsa_cache_append")
+    _check(load().dsa_cache_append(_dev(idx_q, "idx_q", T * IDX_HEADS * IDX_DIM * 2), _dev(idx_k, "idx_k", T * IDX_DIM * 2),
+                                   _dev(ln_gamma, "ln_gamma", IDX_DIM * 4), _dev(ln_beta, "ln_beta", IDX_DIM * 4),
+                                   ln_eps, _dev(q, "q", T * Q_HEADS * QK_DIM * 2), _dev(k, "k", T * KV_HEADS * QK_DIM * 2),
+                                   _dev(v, "v", T * KV_HEADS * V_DIM * 2), Lk, T, rot_idx, rot_main, rope_base,
+                                   _dev(q_idx_out, "q_idx_out", T * IDX_HEADS * IDX_DIM),
+                                   _dev(k_idx_cache, "k_idx_cache", Lk * IDX_DIM),
+                                   _dev(q_out, "q_out", T * Q_HEADS * QK_DIM * 2),
+                                   _dev(k_cache, "k_cache", Lk * KV_HEADS * QK_DIM * 2),
+                                   _dev(v_cache, "v_cache", Lk * KV_HEADS * V_DIM * 2), _stream()), "dsa_cache_append")
     return q_idx_out, q_out
