@@ -70,14 +70,12 @@ __device__ __forceinline__ void rot_table(RotTable& rt, int64_t p, int R, const 
   }
 }
 
-// 8 rotated values of dims d0 .. d0+7 (d0 < R, a multiple of 8): own values x,
-// the pair partners read from the staged row, the table in LDS
-template <class Row>
-__device__ __forceinline__ void rotate8(float (&y)[8], const float (&x)[8], const Row& row, int d0, int R,
-                                        const RotTable& rt) {
-  float xp[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) xp[j] = row(pair_of(d0 + j, R));
+// 8 rotated values of dims d0 .. d0+7 (d0 < R, a multiple of 8) from own
+// values x, their pair partners xp and the table in LDS; kWhole: all 8 dims
+// lie below R (no dim passes through)
+template <bool kWhole = false>
+__device__ __forceinline__ void rot8(float (&y)[8], const float (&x)[8], const float (&xp)[8], int d0, int R,
+                                     const RotTable& rt) {
   const float4 c0 = *reinterpret_cast<const float4*>(&rt.C[d0]);
   const float4 c1 = *reinterpret_cast<const float4*>(&rt.C[d0 + 4]);
   const float4 s0 = *reinterpret_cast<const float4*>(&rt.S[d0]);
@@ -85,7 +83,17 @@ __device__ __forceinline__ void rotate8(float (&y)[8], const float (&x)[8], cons
   const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
   const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) y[j] = d0 + j < R ? fmaf(x[j], c[j], xp[j] * sv[j]) : x[j];
+  for (int j = 0; j < 8; ++j) y[j] = kWhole || d0 + j < R ? fmaf(x[j], c[j], xp[j] * sv[j]) : x[j];
+}
+
+// the same with the partners read one by one from the staged row
+template <class Row>
+__device__ __forceinline__ void rotate8(float (&y)[8], const float (&x)[8], const Row& row, int d0, int R,
+                                        const RotTable& rt) {
+  float xp[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xp[j] = row(pair_of(d0 + j, R));
+  rot8(y, x, xp, d0, R, rt);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(float (&x)[8], const uint4& u) {
@@ -243,7 +251,16 @@ __device__ __forceinline__ void append_kv_head(const AppendArgs& ar, MainShared&
     if (d0 < R) {
       float x[8], y[8];
       unpack_bf16x8(x, own[u]);
-      rotate8(y, x, [&](int j) { return bf16_to_f32(sh.xs[r][j]); }, d0, R, rt);
+      if ((R & 15) == 0) {
+        // R / 2 is a multiple of 8: the piece is rotated whole and its 8
+        // partners are the staged piece R / 2 away
+        float xp[8];
+        const int pd = d0 < (R >> 1) ? d0 + (R >> 1) : d0 - (R >> 1);
+        unpack_bf16x8(xp, *reinterpret_cast<const uint4*>(&sh.xs[r][pd]));
+        rot8<true>(y, x, xp, d0, R, rt);
+      } else {
+        rotate8(y, x, [&](int j) { return bf16_to_f32(sh.xs[r][j]); }, d0, R, rt);
+      }
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
