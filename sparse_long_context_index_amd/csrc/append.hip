@@ -264,7 +264,7 @@ __device__ __forceinline__ void append_kv_head(const AppendArgs& ar, MainShared&
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)f32_to_bf16_rne(y[2 * j]) | ((uint32_t)f32_to_bf16_rne(y[2 * j + 1]) << 16);
+        w[j] = f32x2_to_bf16x2_rne(y[2 * j], y[2 * j + 1]);
       o = make_uint4(w[0], w[1], w[2], w[3]);
     }
     uint16_t* dst = r < kQPerKv ? ar.q_out + ((size_t)t * DSA_Q_HEADS + g * kQPerKv + r) * DSA_QK_DIM

@@ -82,6 +82,13 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(
 // no difference.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// two floats to bf16 (same rounding), a in the low half: one packed conversion
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ __forceinline__ uint32_t* h1_row(const TopkCounters& c, int rep, int t) {
