@@ -95,10 +95,16 @@ static_assert(sizeof(ListShared<4>) == 4 * (8 * 4 * kBufCap + 4 * 4 * kListM), "
 template <int E>
 __device__ __forceinline__ void wave_top_keep(const uint32_t* kk, const uint32_t* ii, const bool* v, bool* keep,
                                               uint32_t* theta) {
+  // Every count is a ballot of one comparison masked by a wave-uniform mask
+  // (a ballot of a compound condition went through a per-lane 0/1 value and
+  // a second comparison: two more VALU instructions per count)
+  uint64_t vm[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) vm[q] = __ballot(v[q]);
   auto count_ge = [&](uint32_t x) {
     uint32_t c = 0;
 #pragma unroll
-    for (int q = 0; q < E; ++q) c += (uint32_t)__popcll(__ballot(v[q] && kk[q] >= x));
+    for (int q = 0; q < E; ++q) c += (uint32_t)__popcll(__ballot(kk[q] >= x) & vm[q]);
     return c;
   };
   // The candidates lie in [lo, hi], so the bits above the highest one in
@@ -128,8 +134,12 @@ __device__ __forceinline__ void wave_top_keep(const uint32_t* kk, const uint32_t
   const uint32_t above = tau == 0xFFFFFFFFu ? 0u : count_ge(tau + 1u);
   const uint32_t r = (uint32_t)kListM - above;             // tau-equal entries to keep
   uint32_t eq = 0;
+  uint64_t em[E];                                          // valid entries equal to tau
 #pragma unroll
-  for (int q = 0; q < E; ++q) eq += (uint32_t)__popcll(__ballot(v[q] && kk[q] == tau));
+  for (int q = 0; q < E; ++q) {
+    em[q] = __ballot(kk[q] == tau) & vm[q];
+    eq += (uint32_t)__popcll(em[q]);
+  }
   uint32_t imax = 0xFFFFFFFFu;                             // keep tau-equal entries with index <= imax
   if (eq > r) {
     uint32_t y = 0;                                        // the r-th largest ~index among them
@@ -138,7 +148,7 @@ __device__ __forceinline__ void wave_top_keep(const uint32_t* kk, const uint32_t
       const uint32_t tr = y | (1u << bit);
       uint32_t cnt = 0;
 #pragma unroll
-      for (int q = 0; q < E; ++q) cnt += (uint32_t)__popcll(__ballot(v[q] && kk[q] == tau && ~ii[q] >= tr));
+      for (int q = 0; q < E; ++q) cnt += (uint32_t)__popcll(__ballot(~ii[q] >= tr) & em[q]);
       if (cnt >= r) y = tr;
     }
     imax = ~y;
