@@ -7,7 +7,10 @@
 // recall[t,h] = exp(lse_sel[t,h] - lse_dense[t,h]): lse_sel comes from the
 // gathered attention over the selected keys (no sink); lse_dense from
 // dense_lse_kernel, a QK-only pass over every visible key:
-//   grid (key chunks of 2,048, KV head g, token t), 4 waves x 512 keys;
+//   grid (KV head g, key chunks of 2,048, token t), 4 waves x 512 keys --
+//   the four heads of a chunk are neighbours in the dispatch order, so the
+//   four slices of a key's K row (1,536 contiguous bytes) are read at about
+//   the same time;
 //   16x16x32 bf16 MFMA with the group's 16 query heads on M and 16 keys on N;
 //   each lane reads 96 contiguous bytes of its key's row (the k-placement of
 //   Q and K agree: lane group q takes dims 48q .. 48q+47), the next block's
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void dense_lse_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ k, int64_t Lk, int T,
                                                         float sm_scale, int n_chunks, float* __restrict__ part) {
   __shared__ float red[4][16][2];
-  const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int g = blockIdx.x, c = blockIdx.y, t = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t p = Lk - T + t;                               // last visible key
@@ -157,7 +160,7 @@ int recall_chunks(int64_t Lk) { return (int)cdiv(Lk, kLseChunk); }
 hipError_t launch_index_recall(const uint16_t* q, const uint16_t* k, int64_t Lk, int T, float sm_scale,
                                const float* lse_sel, float* part, float* recall, float* lse_dense, hipStream_t st) {
   const int nc = recall_chunks(Lk);
-  hipLaunchKernelGGL(dense_lse_kernel, dim3(nc, DSA_KV_HEADS, T), dim3(256), 0, st, q, k, Lk, T, sm_scale, nc, part);
+  hipLaunchKernelGGL(dense_lse_kernel, dim3(DSA_KV_HEADS, nc, T), dim3(256), 0, st, q, k, Lk, T, sm_scale, nc, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(recall_merge_kernel, dim3(T, DSA_Q_HEADS), dim3(64), 0, st, (const float*)part, nc, lse_sel,
