@@ -227,12 +227,17 @@ __device__ __forceinline__ uint32_t count_preceding(const uint32_t* ks, const ui
   return c;
 }
 
-template <int T, bool kLists>
-__global__ __launch_bounds__(256) void idx_scan_kernel(
+// NV: list groups per workgroup (lists only).  Each group of four waves is
+// one list's workgroup of the deal (group v of workgroup x is list NV x + v);
+// with NV = 2 the two lists of a CU run in one workgroup, dispatched together.
+template <int T, bool kLists, int NV = 1>
+__global__ __launch_bounds__(256 * NV) void idx_scan_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, int64_t Lk, float* __restrict__ scores,
     int64_t ld, int64_t ngroups, TopkCounters ctr, int with_hist, ScanLists lists, SeqBatch sb) {
-  int64_t wg = blockIdx.x, G = gridDim.x;                      // this workgroup among its row's, and their number
+  static_assert(NV == 1 || kLists, "list groups only with lists");
+  const int vg = (int)(threadIdx.x >> 8);                       // this wave's list group
+  int64_t wg = (int64_t)blockIdx.x * NV + vg, G = (int64_t)gridDim.x * NV;   // its list among the row's, and their number
   if (!kLists && sb.len) {
     // batch: the sequence b, its keys, queries and score rows
     int b = blockIdx.y;
@@ -280,15 +285,15 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     if (Lk == 0) return;
   }
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* stage = smem;                                        // [4 waves][U*16 rows][kStageRow]
+  uint8_t* stage = smem;                                        // [4 NV waves][U*16 rows][kStageRow]
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + 4 * kScanUnroll * 16 * kStageRow);  // [T][2048]
-  ListShared<T>& ls = *reinterpret_cast<ListShared<T>*>(smem + 4 * kScanUnroll * 16 * kStageRow);
+  ListShared<T>& ls = reinterpret_cast<ListShared<T>*>(smem + 4 * NV * kScanUnroll * 16 * kStageRow)[vg];
   uint32_t bcnt[T], theta[T];                                   // wave buffer fill and threshold per row
 #pragma unroll
   for (int t = 0; t < T; ++t) bcnt[t] = theta[t] = 0u;
   __shared__ uint32_t red_sm[4];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = (threadIdx.x >> 6) & 3;                      // within its list group
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -308,12 +313,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 
   const int64_t last = Lk - 1;
   const int64_t ntiles = cdiv(Lk, 16);
-  uint8_t* st = stage + wave * kScanUnroll * 16 * kStageRow;
+  uint8_t* st = stage + (threadIdx.x >> 6) * kScanUnroll * 16 * kStageRow;
   i32x4 buf[2 * kScanUnroll];
-  // With lists, local tile lt of this workgroup is global tile blockIdx.x +
-  // G * lt and step `it` gives wave w the local tiles 16 it + kScanUnroll w +
-  // u; without, step `it` covers the group of 16 consecutive tiles blockIdx.x
-  // + G * it, kScanUnroll of them per wave.  Load i covers 8 keys of tile i / 2.
+  // With lists, local tile lt of list wg is global tile wg + G * lt and step
+  // `it` gives wave w of its group the local tiles 16 it + kScanUnroll w + u;
+  // without, step `it` covers the group of 16 consecutive tiles blockIdx.x +
+  // G * it, kScanUnroll of them per wave.  Load i covers 8 keys of tile i / 2.
   auto tile_of = [&](int it, int u) -> int64_t {
     if (kLists) return wg + G * ((int64_t)it * 4 * kScanUnroll + wave * kScanUnroll + u);
     return (wg + G * (int64_t)it) * 4 * kScanUnroll + wave * kScanUnroll + u;
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     // sets (128 entries, two per lane, key 0 = empty), compacted into the
     // row's merge area, then each kept entry's rank among them (its place in
     // the list, sorted by key desc, index asc).
-    const uint32_t bx = blockIdx.x, G32 = gridDim.x;
+    const uint32_t bx = (uint32_t)wg, G32 = (uint32_t)G;
     const uint64_t below = (1ull << lane) - 1ull;
     for (int t = wave; t < T; t += 4) {                          // wave-uniform
       uint32_t kk[2], ii[2];
@@ -521,8 +526,12 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
     if (with_hist && scan_list_cap(Lk) >= 65536) return hipErrorInvalidValue;
     const size_t lds = scan_lds_bytes(Lk, T, lists.keys != nullptr) +
                        (with_hist ? (size_t)T * (kHistBins / 2) * sizeof(uint32_t) : 0);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
     const bool with_lists = lists.keys != nullptr;
+    // with several rows an even list grid runs two lists per workgroup (one
+    // workgroup per CU: the two lists of a CU are dispatched together; with
+    // one row the separate workgroups measured faster)
+    const bool pairs = with_lists && T > 1 && grid % 2 == 0;
+    if ((pairs ? 2 * lds : lds) > 160 * 1024) return hipErrorInvalidValue;
     if (with_lists && T > kScanListTMax) return hipErrorInvalidValue;
     switch (T) {
 #define DSA_SCAN_PLAIN(n)                                                                                   \
@@ -530,7 +539,10 @@ hipError_t launch_index_scores(const uint8_t* q_idx, const float* w, const uint8
                      scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{})
 #define DSA_SCAN_CASE(n)                                                                                    \
   case n:                                                                                                   \
-    if (with_lists)                                                                                         \
+    if (with_lists && n > 1 && grid % 2 == 0)                                                               \
+      hipLaunchKernelGGL((idx_scan_kernel<n, true, 2>), dim3((unsigned)(grid / 2)), dim3(512), 2 * lds, st,  \
+                         q_idx, w, k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});      \
+    else if (with_lists)                                                                                    \
       hipLaunchKernelGGL((idx_scan_kernel<n, true>), dim3((unsigned)grid), dim3(256), lds, st, q_idx, w,    \
                          k_idx, Lk, scores, ld, ngroups, ctr, with_hist, lists, SeqBatch{});                \
     else                                                                                                    \
