@@ -198,6 +198,14 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     kc[q] = key_row[cj * nl + l];
     n[q] = lq < nl ? w & 0x7FFFFFFFu : 0u;
     full[q] = lq < nl && (w >> 31) != 0u;
+    // A list's entries past its count hold key 0 (the scan writes them so),
+    // and so do those of a thread without a list, so that below every bound
+    // (L0 and what derives from it, all real keys, at least 1) a test of the
+    // key alone also excludes them.
+    if (lq >= nl) {
+#pragma unroll
+      for (int j = 0; j < kListM; ++j) kA[q][j] = 0u;
+    }
   }
   // the block's entries M, whether any list is capped, the largest key
   // kmax, the smallest cth-th entry xc and the lists nc holding cth entries;
@@ -261,12 +269,12 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       for (int q = 0; q < kLPT; ++q)
 #pragma unroll
         for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
-          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= L0) != 0ull;
+          go = go && __ballot(kA[q][j0] >= L0) != 0ull;
           if (go) {
 #pragma unroll
             for (int j = j0; j < j0 + 8; ++j) {
               const uint32_t u = kA[q][j] - L0;
-              if ((uint32_t)j < n[q] && kA[q][j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
+              if (kA[q][j] >= L0 && (uint32_t)((uint64_t)u >> mshift) == prefix)
                 atomicAdd(&rs.hist[(u >> shift) & mask], 1u);
             }
           }
@@ -278,11 +286,11 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     for (int q = 0; q < kLPT; ++q)
 #pragma unroll
       for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
-        go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= L0) != 0ull;
+        go = go && __ballot(kA[q][j0] >= L0) != 0ull;
         if (go) {
 #pragma unroll
           for (int j = j0; j < j0 + 8; ++j)
-            if ((uint32_t)j < n[q] && kA[q][j] >= L0) atomicAdd(&rs.hist[(kA[q][j] - L0) >> s1], 1u);
+            if (kA[q][j] >= L0) atomicAdd(&rs.hist[(kA[q][j] - L0) >> s1], 1u);
         }
       }
     __syncthreads();
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
     const uint32_t wid = (1u << s1) - 1u;
     const uint32_t hi = lo > 0xFFFFFFFFu - wid ? 0xFFFFFFFFu : lo + wid;
     auto in_b1 = [&](int q, int j) {
-      return (uint32_t)((uint32_t)j < n[q]) & (uint32_t)(kA[q][j] >= lo) & (uint32_t)(kA[q][j] <= hi);
+      return (uint32_t)(kA[q][j] >= lo) & (uint32_t)(kA[q][j] <= hi);
     };
     if (cnt1 <= (uint32_t)kC1Cap) {
       // Few entries in bin b1: the entries above the bin (a prefix of every
@@ -309,11 +317,11 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
         ndq[q] = 0;
 #pragma unroll
         for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
-          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= lo) != 0ull;
+          go = go && __ballot(kA[q][j0] >= lo) != 0ull;
           if (go) {
 #pragma unroll
             for (int j = j0; j < j0 + 8; ++j) {
-              const bool in = (uint32_t)j < n[q] && kA[q][j] >= lo;
+              const bool in = kA[q][j] >= lo;
               ndq[q] += (uint32_t)(in && kA[q][j] > hi);
               nb += (uint32_t)(in && kA[q][j] <= hi);
             }
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
       for (int q = 0; q < kLPT; ++q) {
 #pragma unroll
         for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {   // the entries above the bin lead the list
-          go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= lo) != 0ull;
+          go = go && __ballot(kA[q][j0] >= lo) != 0ull;
           if (go) {
 #pragma unroll
             for (int j = j0; j < j0 + 8; ++j) {
@@ -424,11 +432,11 @@ __global__ __launch_bounds__(kDecNT) void decode_attend_kernel(DecodeArgs d) {
         } else {
 #pragma unroll
           for (int j0 = 0, go = 1; j0 < kListM; j0 += 8) {
-            go = go && __ballot((uint32_t)j0 < n[q] && kA[q][j0] >= tk) != 0ull;
+            go = go && __ballot(kA[q][j0] >= tk) != 0ull;
             if (go) {
 #pragma unroll
               for (int j = j0; j < j0 + 8; ++j)
-                cnt[q] += (uint32_t)((uint32_t)j < n[q] && kA[q][j] >= tk && (kA[q][j] > tk || iA[q][j] <= ti));
+                cnt[q] += (uint32_t)(kA[q][j] >= tk && (kA[q][j] > tk || iA[q][j] <= ti));
             }
           }
         }
