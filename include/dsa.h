@@ -315,9 +315,11 @@ dsa_status dsa_index_recall(const uint16_t* q, const uint16_t* k_cache, const ui
  *
  * Internally the fp8 MFMA contraction only locates candidates: scores of
  * every 64th key give each row a threshold theta; one pass over all keys
- * keeps the keys whose fp8 score reaches theta minus the largest error that
- * score can have (bounded per key from the row's query and weights and the
- * key's norm), up to 12,288 per row; the candidates are
+ * (fp8 logits, head sums on the bf16 matrix cores) keeps the keys whose
+ * approximate score reaches theta minus the largest error that score can
+ * have (bounded per key from the row's query and weights, the key's norm and
+ * the pass's own sum of |weight| x rounded ReLU logit), up to 12,288 per
+ * row; the candidates are
  * re-scored exactly and the top-k selected from them once at least min(k,
  * p_t+1) of them reach theta (then no key left out can belong).  A row that
  * fails this is recomputed exactly on the device, so the result never

@@ -14,6 +14,14 @@
 // 8 products after aligning them to the group's largest exponent, so its sums
 // carry less precision than fp32 (measured and bounded in the tests).
 //
+// The candidate pass of the fused prefill top-k (kGemmCand) needs no scores,
+// only a test against the row threshold with a proven margin, so it does the
+// head sums on the bf16 matrix cores instead (gemm_block_cand): the VALU is
+// what bounds the score modes (about 76 instructions per block of 8 MFMAs,
+// issued while the matrix cores idle), and the candidate mode's blocks take
+// 32.  Its candidates are recorded as per-lane bit masks over windows of 32
+// blocks and emitted once per window, as key indices only.
+//
 // Built with MFMA results in VGPRs (no accumulation-register reads).
 #include <type_traits>
 
@@ -70,6 +78,83 @@ __device__ __forceinline__ float2 gemm_block(const i32x8 (&a)[8], const float* w
     if (key > p0 + grp + 4) hi = -INFINITY;
   }
   return make_float2(lo, hi);
+}
+
+// Candidate mode: the same 8 fp8 MFMA tiles, and the ReLU-weighted head sums
+// on the matrix cores instead of the VALU.  The 32 logits a lane holds (heads
+// 4 grp .. + 3 of its key for 8 tokens) are rounded to bf16 two at a time and
+// clamped at zero as 16-bit integers (ReLU commutes with the rounding), which
+// is exactly the B operand layout of a 16x16x32 bf16 MFMA whose k runs over
+// (token pair, head); four such MFMAs against a block-diagonal weight operand
+// (aw, fixed for the kernel) leave in lane (key, grp) the rows 4 grp + i:
+// i = 0 / 1 the score of token grp / grp + 4, i = 2 / 3 the bound term
+// sum_h |w_h| R_h of the same tokens (R_h the rounded ReLU logit).  Per block
+// this takes 32 VALU instructions where the VALU epilogue takes 76, for four
+// bf16 MFMAs; the bf16 rounding of R and w costs at most 2^-7 (1.012) of
+// sum_h |w_h| R_h, which the candidate test adds to its margin.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t relu_bf16x2(float a, float b) {
+  const i16x2 v = __builtin_bit_cast(i16x2, f32x2_to_bf16x2_rne(a, b));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, i16x2{0, 0}));
+}
+
+// The weight operands of the head-sum MFMAs: row m = 4 g + i holds the
+// weights (i < 2) or their magnitudes (i >= 2) of token tm = g + 4 (i & 1),
+// in MFMA tm / 2 and the k-half tm % 2 of its lane group's heads; every other
+// entry is zero, so each output row sums one token's 16 heads exactly once.
+__device__ __forceinline__ void cand_weight_operands(const float* w, int t0, int T, int col, int grp,
+                                                     bf16x8 (&aw)[4]) {
+  const int tm = (col >> 2) + 4 * (col & 1);
+  const int t = t0 + tm < T ? t0 + tm : T - 1;
+  const float* wp = w + (size_t)t * 16 + 4 * grp;
+  uint32_t w01 = f32x2_to_bf16x2_rne(wp[0], wp[1]);
+  uint32_t w23 = f32x2_to_bf16x2_rne(wp[2], wp[3]);
+  if (col & 2) {
+    w01 &= 0x7FFF7FFFu;
+    w23 &= 0x7FFF7FFFu;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool mine = q == (tm >> 1);
+    const bool hi = (tm & 1) != 0;
+    const u32x4 v = u32x4{mine && !hi ? w01 : 0u, mine && !hi ? w23 : 0u, mine && hi ? w01 : 0u,
+                          mine && hi ? w23 : 0u};
+    aw[q] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <class Reload>
+__device__ __forceinline__ f32x4 gemm_block_cand(const i32x8 (&a)[8], const bf16x8 (&aw)[4], i32x8& slot,
+                                                 Reload reload, int64_t kk, int t0, int64_t Lk, int T, int col,
+                                                 int grp) {
+  const int64_t p0 = Lk - T + t0;                       // position of the wave's first token
+  const i32x8 b = slot;
+  f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two halves of four tokens: each half's logits feed two head-sum MFMAs,
+  // so only four logit tiles are live at a time
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = mfma_f8_16x16x128(a[4 * hf + j], b, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (hf == 1) slot = reload();                       // the MFMAs have read the slot
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 r = u32x4{relu_bf16x2(c[2 * q][0], c[2 * q][1]), relu_bf16x2(c[2 * q][2], c[2 * q][3]),
+                            relu_bf16x2(c[2 * q + 1][0], c[2 * q + 1][1]),
+                            relu_bf16x2(c[2 * q + 1][2], c[2 * q + 1][3])};
+      d = mfma_bf16_16x16x32(aw[2 * hf + q], __builtin_bit_cast(bf16x8, r), d);
+    }
+  }
+  if (kk + 15 > p0) {                                   // the block reaches the causal edge (wave-uniform)
+    const int64_t key = kk + col;
+    if (key > p0 + grp) d[0] = -INFINITY;
+    if (key > p0 + grp + 4) d[1] = -INFINITY;
+  }
+  return d;
 }
 
 // A round's 8 x 64 scores, staged in the wave's LDS rows, leave as 16-byte
@@ -171,6 +256,16 @@ __device__ __forceinline__ float cand_threshold(uint32_t theta) {
 
 enum GemmMode { kGemmScores = 0, kGemmSample = 1, kGemmCand = 2 };
 
+// Candidate mode: margin factor for the bf16 head sums, applied to
+// sum_h |w_h| R_h.  Rounding w and R to bf16 (unit roundoff 2^-8 each, both
+// round to nearest even) moves a term w_h R_h by at most 2^-8 |w_h| R_h +
+// 2^-8 |w_h| relu(l_h) <= 2^-7 (1 - 2^-8)^-2 |w~_h| R_h, the MFMA's exact
+// products and fp32 sums add below 2^-19 of the same sum, and the computed
+// sum of |w~_h| R_h is within 2^-19 of its exact value: 1/100 covers
+// 2^-7 x 1.012 with a 26% margin.  The fp8 contraction's own error stays in
+// the per-row factor cw (times the key norm bound).
+constexpr float kCandRound = 0.01f;
+
 struct GemmArgs {
   const float* cw;     // candidate mode: [T] per-row error factor (see PrefillCand)
   const float* knorm;  // candidate mode: [Lk] key norm bounds
@@ -244,15 +339,20 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
   }
   if (t0 >= T) return;                                 // wave-uniform
 
-  // the wave's 8 x 16 head weights sit in LDS (registers go to the operands)
-  __shared__ __attribute__((aligned(16))) float wsm[4][8 * 16];
-  {
+  // score modes: the wave's 8 x 16 head weights sit in LDS (registers go to
+  // the operands); candidate mode: the head-sum MFMAs' weight operands
+  constexpr bool kCand = kMode == kGemmCand;
+  __shared__ __attribute__((aligned(16))) float wsm[kCand ? 1 : 4][kCand ? 1 : 8 * 16];
+  const float* wv = wsm[kCand ? 0 : wave];
+  bf16x8 aw[4];
+  if constexpr (kCand) {
+    cand_weight_operands(ga.w, t0, T, col, grp, aw);
+  } else {
     const int j = lane >> 3, h = 2 * (lane & 7);
     const int t = t0 + j < T ? t0 + j : T - 1;
     wsm[wave][j * 16 + h] = ga.w[t * 16 + h];
     wsm[wave][j * 16 + h + 1] = ga.w[t * 16 + h + 1];
   }
-  const float* wv = wsm[wave];
   i32x8 a[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -266,7 +366,7 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
   const bool tail = (s0 + kGemmKeys) * step > Lk;      // wave-uniform
   const uint8_t* kp = ga.k_idx + (s0 + col) * step * 128 + 32 * grp;
   constexpr int NB = kGemmKeys / 16;
-  static_assert(NB % PF == 0 && PF <= kGemmPF, "whole prefetch rounds");
+  static_assert(NB % PF == 0 && PF <= kGemmPF && 32 % PF == 0, "whole prefetch rounds and candidate windows");
   const int64_t end = ga.nkeys - s0 < kGemmKeys ? ga.nkeys - s0 : kGemmKeys;   // keys of this tile
   __shared__ __attribute__((aligned(16))) float stage[kMode == kGemmCand ? 1 : 4][8 * kStageStride];
   float* st = stage[kMode == kGemmCand ? 0 : wave];
@@ -301,38 +401,63 @@ __global__ __launch_bounds__(256, GemmShape<kMode>::waves) void idx_gemm_kernel(
     i32x8 b[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u) b[u] = load_b(u);
+    // candidate mode: bit i of bm0 / bm1 marks block wb + i of the current
+    // 32-block window as holding a candidate of token grp / grp + 4 in this
+    // lane's key column; a window's keys are emitted together (the indices
+    // only: the exact pass that follows rescores every candidate)
+    uint32_t bm0 = 0, bm1 = 0;
+    auto flush_window = [&](int wb) {
+      uint2* lb = lcand[kCand ? wave : 0];
+      for (;;) {
+        const bool e0 = bm0 != 0u, e1 = bm1 != 0u;
+        const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
+        if (!(m0 | m1)) break;                           // wave-uniform
+        const uint32_t key0 = (uint32_t)(s0 + (wb + (e0 ? __builtin_ctz(bm0) : 0)) * 16 + col);
+        const uint32_t key1 = (uint32_t)(s0 + (wb + (e1 ? __builtin_ctz(bm1) : 0)) * 16 + col);
+        bm0 &= bm0 - 1u;
+        bm1 &= bm1 - 1u;
+        if (m0) emit_local(e0, m0, grp, lane, c0, lb + grp * kLocalCand, t0 + grp, 0u, key0, ga.cand);
+        if (m1) emit_local(e1, m1, grp, lane, c1, lb + (grp + 4) * kLocalCand, t0 + grp + 4, 0u, key1, ga.cand);
+      }
+    };
+    int kb = 0;
 #pragma unroll 1
-    for (int kb = 0; kb < NB; kb += PF) {
+    for (; kb < NB; kb += PF) {
       if ((int64_t)kb * 16 >= end) break;                // wave-uniform
+      float nr[PF];                                      // candidate mode: the round's key norm bounds
+      if constexpr (kCand) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) nr[u] = nsm[(kb + u) * 16 + col];
+      }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int nb = kb + PF + u;
         const int64_t kk = (s0 + (kb + u) * 16) * step;
         // the next fragment of this slot is loaded unconditionally (no branch around the load)
-        const float2 v = gemm_block(a, wv, b[u], [&] { return load_b(nb < NB ? nb : NB - 1); }, kk, step, t0, Lk,
-                                    T, col, grp);
-        if (kMode == kGemmCand) {
-          // a key is a candidate of token t when its score reaches t's
-          // threshold: masked keys score -inf, which no threshold admits, and
-          // tokens beyond T have threshold +inf
-          const int64_t key = kk + col;
-          const float ncur = nsm[(kb + u) * 16 + col];
-          const bool ok0 = v.x + cw0 * ncur >= th0, ok1 = v.y + cw1 * ncur >= th1;
-          const uint32_t k0 = order_key(v.x), k1 = order_key(v.y);
-          const uint64_t m0 = __ballot(ok0), m1 = __ballot(ok1);
-          if (m0 | m1) {                                 // wave-uniform
-            uint2* lb = lcand[kMode == kGemmCand ? wave : 0];
-            emit_local(ok0, m0, grp, lane, c0, lb + grp * kLocalCand, t0 + grp, k0, (uint32_t)key, ga.cand);
-            emit_local(ok1, m1, grp, lane, c1, lb + (grp + 4) * kLocalCand, t0 + grp + 4, k1, (uint32_t)key,
-                       ga.cand);
-          }
+        auto next = [&] { return load_b(nb < NB ? nb : NB - 1); };
+        if constexpr (kCand) {
+          // a key is a candidate of token t when its score plus both error
+          // margins reaches t's threshold: masked keys score -inf, which no
+          // threshold admits, and tokens beyond T have threshold +inf
+          const f32x4 d = gemm_block_cand(a, aw, b[u], next, kk, t0, Lk, T, col, grp);
+          const bool ok0 = fmaf(kCandRound, d[2], fmaf(cw0, nr[u], d[0])) >= th0;
+          const bool ok1 = fmaf(kCandRound, d[3], fmaf(cw1, nr[u], d[1])) >= th1;
+          const uint32_t bit = 1u << ((kb + u) & 31);
+          bm0 |= ok0 ? bit : 0u;
+          bm1 |= ok1 ? bit : 0u;
         } else {
+          const float2 v = gemm_block(a, wv, b[u], next, kk, step, t0, Lk, T, col, grp);
           st[grp * kStageStride + 16 * u + col] = v.x;
           st[(grp + 4) * kStageStride + 16 * u + col] = v.y;
         }
       }
-      if (kMode != kGemmCand) store_round(st, s0 + kb * 16, t0, ga.nkeys, T, ga.scores, ga.ld, col, grp);
+      if constexpr (kCand) {
+        if (((kb + PF) & 31) == 0) flush_window(kb + PF - 32);
+      } else {
+        store_round(st, s0 + kb * 16, t0, ga.nkeys, T, ga.scores, ga.ld, col, grp);
+      }
     }
+    if constexpr (kCand) flush_window(kb & ~31);         // a window cut short by the tile's end
   };
   if (tail)
     main_loop(std::true_type{});

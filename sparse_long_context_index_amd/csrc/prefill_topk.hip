@@ -18,8 +18,9 @@
 //     error relative to sum_h |w_h| sum_d |q_hd k_d| = u . |k|, which
 //     Cauchy-Schwarz bounds by |u| |k|);
 //  3. the contraction over all keys appends every visible key s whose score
-//     plus c_t n_s reaches theta to the row's slots: no key whose exact score
-//     reaches theta is missed;
+//     plus c_t n_s plus 0.01 sum_h |w_h| R_h reaches theta to the row's slots
+//     (the last term covers the bf16 head sums of this pass, R_h its rounded
+//     ReLU logits): no key whose exact score reaches theta is missed;
 //  4. prefill_rescore_kernel recomputes the candidates' scores exactly;
 //  5. prefill_refine_kernel checks that at least min(k, visible keys)
 //     candidates reach theta on their exact scores -- then every key left out
