@@ -16,9 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "index_scores.hip", "prefill_scores.hip", "prefill_topk.hip", "topk.hip", "attn.hip", "decode.hip", "append.hip", "recall.hip"]
-# per-source extra flags: the prefill contraction keeps its MFMA results in
-# VGPRs, which saves the accumulation-register reads of its epilogue
-EXTRA = {"prefill_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the prefill contraction and the gathered attention
+# keep their MFMA results in VGPRs, which saves the accumulation-register
+# reads and writes around their epilogues (the attention's online softmax
+# rescales its output tiles on the VALU)
+EXTRA = {"prefill_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

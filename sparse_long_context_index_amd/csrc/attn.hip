@@ -106,11 +106,11 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int n_chunk
   if (M != -INFINITY) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const float f = mc[c] == -INFINITY ? 0.f : exp2f(mc[c] - M);
+      const float f = mc[c] == -INFINITY ? 0.f : exp2_hw(mc[c] - M);
       L += f * lc[c];
       O += f * oc[c];
     }
-    if (a.sink) L += exp2f(s2 - M);
+    if (a.sink) L += exp2_hw(s2 - M);
   }
   const float outv = (M != -INFINITY && L > 0.f) ? O / L : 0.f;
   a.out[((size_t)t * 64 + h) * 128 + dv] = f32_to_bf16_rne(outv);

@@ -46,6 +46,12 @@ struct Window {
   }
 };
 
+// 2^x on the exp unit (v_exp_f32): 1 for 0, 0 for -inf, results below the
+// smallest normal float flushed to zero -- a softmax term that small is below
+// 2^-126 of its row's largest term (which is 1) and cannot change a sum of
+// them by a float ulp
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Orders a wave's LDS accesses before and after this point (compiler and
 // hardware: a wave's LDS operations complete in order).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -172,13 +178,15 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
       const float mn = fmaxf(m, mx);
       const bool dead = mn == -INFINITY;
-      const float alpha = dead ? 1.0f : exp2f(m - mn);
+      // before a wave's first tile its running sums are zero: nothing to rescale
+      const bool rescale = rd > 0;                  // wave-uniform
+      const float alpha = (dead || !rescale) ? 1.0f : exp2_hw(m - mn);
       float ps = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = dead ? 0.0f : exp2f(z[b][i] - mn);
+          const float pv = dead ? 0.0f : exp2_hw(z[b][i] - mn);
           ps += pv;
           const __bf16 hi = (__bf16)pv;
           pf[b * 4 + i] = hi;
@@ -187,11 +195,13 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       lsum = lsum * alpha + ps;
       m = mn;
       // rescale O rows (heads 4*kg + i) by their column's alpha
+      if (rescale) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float al = __shfl(alpha, 4 * kg + i, 64);
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * kg + i, 64);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) o[b][i] *= al;
+          for (int b = 0; b < 8; ++b) o[b][i] *= al;
+        }
       }
     }
     // the V staging area is the wave's own: its stores precede its reads
@@ -256,7 +266,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = M == -INFINITY ? 0.f : exp2f(mwv[w] - M);
+      const float f = M == -INFINITY ? 0.f : exp2_hw(mwv[w] - M);
       L += f * lwv[w];
       O += f * owv[w];
     }
@@ -274,11 +284,11 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       if (a.sink) {
         const float s2 = sinkv[q] * kLog2e;
         Mf = fmaxf(M, s2);
-        sl = exp2f(s2 - Mf);
+        sl = exp2_hw(s2 - Mf);
       }
       float outv = 0.f, lse = -INFINITY;
       if (Mf != -INFINITY) {
-        const float sc = M == -INFINITY ? 0.f : exp2f(M - Mf);
+        const float sc = M == -INFINITY ? 0.f : exp2_hw(M - Mf);
         const float Lf = L * sc + sl;
         outv = Lf > 0.f ? (O * sc) / Lf : 0.f;
         lse = (Mf + log2f(Lf)) * kLn2;
