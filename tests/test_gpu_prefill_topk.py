@@ -116,6 +116,21 @@ def test_prefill_topk_misleading_sample(dev):
     run_case(dev, d, cfg.Lk, cfg.T, cfg.k, oracle_rows=(0, 9))
 
 
+def test_prefill_topk_weights_at_bf16_midpoints(dev):
+    # The candidate pass sums the heads with weights and ReLU logits rounded to
+    # bf16.  Weights of alternating sign, each just off a bf16 rounding
+    # midpoint, make those rounding errors large next to the scores (which
+    # mostly cancel), so the pass's margin for them decides which keys are
+    # candidates; the selection must still equal the exact one.
+    cfg = synth.DecodeConfig("b", L=40000, T=12, k=2048, plant_frac=0.01, seed=21)
+    d = synth.decode_inputs(cfg, with_kv=False)
+    rng = np.random.default_rng(21)
+    grid = 1.0 + rng.integers(0, 127, size=(cfg.T, 16)) / 128.0      # bf16 values in [1, 2)
+    off = np.where(np.arange(16) % 2 == 0, 1 - 2.0 ** -12, 1 + 2.0 ** -12) * 2.0 ** -8
+    d["w"] = (np.where(np.arange(16) % 2 == 0, 1.0, -1.0) * (grid + off)).astype(np.float32)
+    run_case(dev, d, cfg.Lk, cfg.T, cfg.k, oracle_rows=(0, 5, 11))
+
+
 def test_prefill_topk_workspace_reuse(dev):
     cfg = synth.DecodeConfig("w", L=30000, T=24, k=512, plant_frac=0.01, seed=5)
     d = synth.decode_inputs(cfg, with_kv=False)
