@@ -91,15 +91,17 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
   // sink logits of the heads this thread writes, loaded now with the queries
   // (read after the combine they would add a round trip at the very end).
   // Without a sink the loads read the query instead and are discarded.
-  constexpr int R = NW * 64 / 128;             // heads covered per pass
-  constexpr int Q = GH / R;                    // passes
-  static_assert(NW * 64 % 128 == 0 && GH % R == 0, "combine layout");
-  const int h0 = (threadIdx.x >> 7) & (R - 1);
-  float sinkv[Q];
+  // Pass p of thread i combines head (p NC + i) / 32, dims 4 ((p NC + i) % 32)
+  // .. + 3, NC = NW * 64 threads.
+  constexpr int NC = NW * 64;
+  constexpr int P = GH * 32 / NC;              // passes
+  static_assert(GH * 32 % NC == 0, "combine layout");
+  const int ci = (int)(threadIdx.x & (NC - 1));
+  float sinkv[P];
   {
-    const float* sp = a.sink ? a.sink + g * GH + h0 : reinterpret_cast<const float*>(a.q);
+    const float* sp = a.sink ? a.sink + g * GH : reinterpret_cast<const float*>(a.q);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) sinkv[q] = sp[R * q];
+    for (int p = 0; p < P; ++p) sinkv[p] = sp[(p * NC + ci) >> 5];
   }
 
   f32x4 o[8];
@@ -245,67 +247,82 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
   __syncthreads();
   if (threadIdx.x >= NW * 64) return;
 
-  // every thread combines outputs (head hc, dim dv) for hc = h0 + R*q; all
-  // LDS reads are issued before any result is written
+  // every thread combines, per pass, four dims of one head from the NW wave
+  // partials: all LDS reads (16-byte pieces for the outputs) are issued
+  // before any result is written
   const int unit = t * HKV + g;
-  const int dv = threadIdx.x & 127;
-  float Mq[Q], Lq[Q], Oq[Q];
+  float Mp[P], Lp[P];
+  float4 Op[P];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int hc = h0 + R * q;
-    float mwv[NW], lwv[NW], owv[NW];
+  for (int p = 0; p < P; ++p) {
+    const int idx = p * NC + ci;
+    const int hc = idx >> 5, dq = (idx & 31) * 4;
+    float mwv[NW], lwv[NW];
+    float4 owv[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       mwv[w] = mw[w * 16 + hc];
       lwv[w] = lw[w * 16 + hc];
-      owv[w] = ow[(w * 16 + hc) * 128 + dv];
+      owv[w] = *reinterpret_cast<const float4*>(ow + (w * 16 + hc) * 128 + dq);
     }
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, mwv[w]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float f = M == -INFINITY ? 0.f : exp2_hw(mwv[w] - M);
       L += f * lwv[w];
-      O += f * owv[w];
+      O.x += f * owv[w].x;
+      O.y += f * owv[w].y;
+      O.z += f * owv[w].z;
+      O.w += f * owv[w].w;
     }
-    Mq[q] = M;
-    Lq[q] = L;
-    Oq[q] = O;
+    Mp[p] = M;
+    Lp[p] = L;
+    Op[p] = O;
   }
   if (n_chunks == 1) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int h = g * GH + h0 + R * q;
-      const float M = Mq[q], L = Lq[q], O = Oq[q];
+    for (int p = 0; p < P; ++p) {
+      const int idx = p * NC + ci;
+      const int hc = idx >> 5, dq = (idx & 31) * 4;
+      const int h = g * GH + hc;
+      const float M = Mp[p], L = Lp[p];
       float Mf = M;
       float sl = 0.f;
       if (a.sink) {
-        const float s2 = sinkv[q] * kLog2e;
+        const float s2 = sinkv[p] * kLog2e;
         Mf = fmaxf(M, s2);
         sl = exp2_hw(s2 - Mf);
       }
-      float outv = 0.f, lse = -INFINITY;
+      float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+      float Lf = 0.f;
       if (Mf != -INFINITY) {
         const float sc = M == -INFINITY ? 0.f : exp2_hw(M - Mf);
-        const float Lf = L * sc + sl;
-        outv = Lf > 0.f ? (O * sc) / Lf : 0.f;
-        lse = (Mf + log2f(Lf)) * kLn2;
+        Lf = L * sc + sl;
+        if (Lf > 0.f) {
+          const float inv = sc / Lf;                        // one division for the four dims
+          r = make_float4(Op[p].x * inv, Op[p].y * inv, Op[p].z * inv, Op[p].w * inv);
+        }
       }
-      a.out[((size_t)t * 64 + h) * 128 + dv] = f32_to_bf16_rne(outv);
-      if (a.lse && dv == 0) a.lse[(size_t)t * 64 + h] = lse;
+      *reinterpret_cast<uint2*>(a.out + ((size_t)t * 64 + h) * 128 + dq) =
+          make_uint2(f32x2_to_bf16x2_rne(r.x, r.y), f32x2_to_bf16x2_rne(r.z, r.w));
+      if (a.lse && (idx & 31) == 0)
+        a.lse[(size_t)t * 64 + h] = Mf == -INFINITY ? -INFINITY : (Mf + log2f(Lf)) * kLn2;
     }
   } else {
     float* pp = part + ((size_t)unit * n_chunks + c) * kPartFloats;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int hc = h0 + R * q;
-      if (dv == 0) {
-        pp[hc] = Mq[q];
-        pp[16 + hc] = Lq[q];
+    for (int p = 0; p < P; ++p) {
+      const int idx = p * NC + ci;
+      const int hc = idx >> 5, dq = (idx & 31) * 4;
+      if ((idx & 31) == 0) {
+        pp[hc] = Mp[p];
+        pp[16 + hc] = Lp[p];
       }
-      pp[32 + hc * 128 + dv] = Oq[q];
+      *reinterpret_cast<float4*>(pp + 32 + hc * 128 + dq) = Op[p];
     }
   }
 }
