@@ -52,6 +52,15 @@ struct Window {
 // them by a float ulp
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ds_read_b64_tr_b16 (gfx950): a transposing 8-byte LDS read, see the P.V
+// operand below for its lane layout (measured on the hardware with distinct
+// values in every LDS element); p must be an 8-byte aligned LDS address
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+}
+
 // Orders a wave's LDS accesses before and after this point (compiler and
 // hardware: a wave's LDS operations complete in order).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -211,15 +220,21 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
     // holds this wave for the slowest wave's loads
     wave_lds_sync();
     if (active) {
-      // ---- PV: B operand = V[key(kg,e)][16*blk + col], key(kg,e) = e<4 ? 4kg+e : 12+4kg+e
+      // ---- PV: B operand = V[key(kg,e)][16*blk + col], key(kg,e) = e<4 ? 4kg+e : 12+4kg+e.
+      // Two LDS transpose reads per 16-dim block: in each 16-lane group,
+      // ds_read_b64_tr_b16 gives lane i, element s, element i % 4 of the 8
+      // bytes that lane i / 4 + 4 s of the group addresses; lane q of group kg
+      // addresses dims 4 (q % 4) .. + 3 of key row 4 kg + q / 4 (keys 0-15)
+      // and the same 16 rows down (keys 16-31), so lane (kg, col) receives
+      // V[4 kg + s][16 blk + col] and V[16 + 4 kg + s][16 blk + col].
+      const int tq = lane & 15;
+      const uint16_t* vr = vs + (4 * kg + (tq >> 2)) * kVStride + 4 * (tq & 3);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        u16x8 vb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = e < 4 ? 4 * kg + e : 12 + 4 * kg + e;
-          vb[e] = vs[kk * kVStride + blk * 16 + col];
-        }
+        const s16x4 lo = lds_read_tr16(vr + blk * 16);
+        const s16x4 hi = lds_read_tr16(vr + 16 * kVStride + blk * 16);
+        const u16x8 vb = u16x8{(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                               (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
         o[blk] = mfma_bf16_16x16x32(pf, __builtin_bit_cast(bf16x8, vb), o[blk]);
         o[blk] = mfma_bf16_16x16x32(pl, __builtin_bit_cast(bf16x8, vb), o[blk]);
       }
