@@ -155,15 +155,8 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
       for (int i = 0; i < 8; ++i)
         vraw[i] = *reinterpret_cast<const u16x8*>(a.v + ((size_t)(rv[i] >= 0 ? rv[i] : 0) * HKV + g) * 128 +
                                                   8 * (lane & 15));
-      // ---- stage V rows (an empty slot stages zeros, never the row it loaded)
-      {
-        const u16x8 zero = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<u16x8*>(vs + (4 * i + (lane >> 4)) * kVStride + 8 * (lane & 15)) =
-              rv[i] >= 0 ? vraw[i] : zero;
-      }
-      // ---- QK for the two 16-key blocks
+      __builtin_amdgcn_sched_barrier(0);   // every load leaves before the QK (the scheduler would delay V's)
+      // ---- QK for the two 16-key blocks (waits for the K rows only)
       f32x4 acc[2];
       uint64_t valid[2];
 #pragma unroll
@@ -213,6 +206,19 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Src& src, 
 #pragma unroll
           for (int b = 0; b < 8; ++b) o[b][i] *= al;
         }
+      }
+      // ---- stage V rows, after QK and the softmax so that those need not
+      // wait for them (the V loads are issued last).  An empty slot stages
+      // zeros, never the row it loaded: the row is ANDed with a mask that an
+      // empty asm hides from the compiler, since a select between the loaded
+      // row and zeros let it move that load into a branch followed by a wait
+      // for every outstanding load, ahead of the QK.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int msk = rv[i] >= 0 ? -1 : 0;
+        asm volatile("" : "+v"(msk));
+        *reinterpret_cast<i32x4*>(vs + (4 * i + (lane >> 4)) * kVStride + 8 * (lane & 15)) =
+            __builtin_bit_cast(i32x4, vraw[i]) & msk;
       }
     }
     // the V staging area is the wave's own: its stores precede its reads
