@@ -17,12 +17,14 @@
 //        MFMA chains (keys x head-columns), 6 k-steps over qk dim 192;
 //   softmax: online, base-2, per head column, fp32;
 //   PV : P (heads x 32 keys) is already in A-operand order; V rows are staged
-//        through LDS and read as the B operand, 8 MFMAs over v dim 128 for
-//        each of P's two bf16 parts (high, and the rounding remainder), so
-//        the products keep ~16 bits of every probability.
-// Empty slots (idx < 0, idx >= Lk, positions past the window) load no value
-// row: their V lanes are written as zeros and their logits as -inf, so
-// poisoned cache rows outside the set can never reach the output.
+//        through LDS (after the QK and the softmax, which wait for the K rows
+//        only) and read as the B operand, 8 MFMAs over v dim 128 for each of
+//        P's two bf16 parts (high, and the rounding remainder), so the
+//        products keep ~16 bits of every probability.
+// Empty slots (idx < 0, idx >= Lk, positions past the window) read a clamped
+// valid row but use none of it: their V lanes are staged as zeros and their
+// logits set to -inf, so poisoned cache rows outside the set can never reach
+// the output.
 #include "attn_core.hpp"
 #include "dsa_common.hpp"
 #include "kernels.hpp"
