@@ -295,6 +295,32 @@ def test_sparse_attention_skips_out_of_range_and_empty_rows(dev):
     assert np.all(np.isneginf(lse2.cpu().numpy()[2]))
 
 
+@pytest.mark.parametrize("T", [1, 256])
+def test_sparse_attention_empty_slots_over_poisoned_row_zero(dev, T):
+    """Empty slots (-1) read the clamped row 0 and must use none of it: row 0
+    is NaN-poisoned and never selected, and every 32-key tile holds empty
+    slots, in the split path (T = 1: key chunks merged afterwards) and the
+    single-chunk path (T = 256: 1,024 units)."""
+    rng = np.random.default_rng(77 + T)
+    Lk, k = 6000, 2048
+    q, K, V = bf16(rng, (T, 64, 192)), bf16(rng, (Lk, 4, 192)), bf16(rng, (Lk, 4, 128))
+    sink = rng.standard_normal(64).astype(np.float32)
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        sel = np.sort(rng.choice(np.arange(1, Lk), size=k // 2, replace=False)).astype(np.int32)
+        idx[t, 0::2] = sel                                   # every other slot empty
+    keep = np.unique(idx[idx >= 0])
+    assert 0 not in keep
+    Kp, Vp = poison_except(K, V, keep)
+    sc = float(np.float32(1 / math.sqrt(192)))
+    out = binding.sparse_gqa_attn(g(q, dev), g(Kp, dev), g(Vp, dev), Lk, g(idx, dev), g(sink, dev), sc)
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    o_ref, _ = oracle.sparse_attention(q, K, V, idx, sink, sc)
+    ok, msg = oracle.attn_check(o, o_ref)
+    assert ok, msg
+
+
 # ------------------------------------------------------------ SWA
 
 @pytest.mark.parametrize("window", [128, 1, 37, 200])
